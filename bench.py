@@ -1,0 +1,358 @@
+#!/usr/bin/env python3
+"""Benchmark of the transfer hot path on one MI355X (gfx950).
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  1. source-slice rotation (host arithmetic, tb_rotate_sources),
+  2. the two-source fp32 reduce-copy over 256 MiB buffers (tb_reduce_copy),
+  3. the 47,520-copy batched scattered copy into a 4 GiB pool (tb_batched_copy),
+all enqueued on one stream.  Inputs are prepared (and resident in HBM) before
+the timed region; K steps are enqueued behind the spin gate with a HIP event
+at every kernel boundary, so each launch is timed on the stream it runs on.
+
+Default output is ONE JSON line:
+  value        whole-step throughput, algorithmic HBM GB/s (decimal):
+               (N+1) x numBytes for the reduce-copy + 2 x sum(bytes) for the batch
+  roofline     the dominant kernel (the reduce-copy) against 8 TB/s HBM
+  cpu_baseline the oracle timed on one host core over the same step
+--suite additionally prints one line per configuration (C1-C5, sweep).
+"""
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "HBM GB/s & % of peak (rotated reduce-copy); GB/s + copies/s (batched scatter)"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
+GATE_TIMEOUT_MS = 20000
+
+
+def _sha256(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, only
+    if it was taken on the kernels as they are now (same source hash)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    src = os.path.join(ROOT, "copy_reduce_amd", "csrc", "tb_kernels.hip")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != _sha256(src):
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+class Timed:
+    """Enqueue a sequence of launches behind the spin gate with an event at
+    every boundary; per-launch milliseconds come from consecutive events."""
+
+    def __init__(self, torch, tb, stream):
+        self.torch, self.tb, self.stream = torch, tb, stream
+
+    def run(self, launches):
+        torch, tb, s = self.torch, self.tb, self.stream
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        tb.tb_spin_gate_arm(GATE_TIMEOUT_MS, s.cuda_stream)
+        evs[0].record(s)
+        for j, fn in enumerate(launches):
+            fn()
+            evs[j + 1].record(s)
+        tb.tb_spin_gate_release()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        if tb.tb_spin_gate_status() != tb.TB_OK:
+            raise RuntimeError("spin gate timed out: the timed launches were not gated")
+        ms = [evs[j].elapsed_time(evs[j + 1]) for j in range(len(launches))]
+        return ms, evs[0].elapsed_time(evs[-1]), wall
+
+
+# ---------------------------------------------------------------------------
+# workload set-up (untimed)
+# ---------------------------------------------------------------------------
+
+def setup_reduce(torch, w):
+    from copy_reduce_amd.torch_api import RotatedSources
+    rs = RotatedSources(w.nsrc, w.nfloats, w.rotate_bytes, fill=w.fill)
+    dst = torch.zeros(max(1, w.nfloats), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    return rs, dst
+
+
+def setup_batch(torch, tb, batch, rotate_bytes):
+    """K_b source replicas (the slice-count rule over the batch's source bytes)
+    and one descriptor array per replica; pool pre-filled with 0xA5."""
+    import workloads as wl
+    from copy_reduce_amd.torch_api import make_desc
+    kb = tb.tb_num_slices(batch.total_bytes, rotate_bytes)
+    stride = tb.tb_slice_stride(batch.src_bytes)
+    src = torch.empty(max(1, kb * stride), dtype=torch.uint8, device="cuda")
+    host = torch.from_numpy(batch.payload).pin_memory()
+    for r in range(kb):
+        src[r * stride:r * stride + batch.src_bytes].copy_(host, non_blocking=True)
+    pool = torch.full((batch.pool_bytes,), wl.POOL_FILL, dtype=torch.uint8, device="cuda")
+    base = int(src.data_ptr())
+    descs = {base + r * stride: make_desc(batch.desc, base + r * stride, int(pool.data_ptr()))
+             for r in range(kb)}
+    torch.cuda.synchronize()
+    return {"kb": kb, "stride": stride, "src": src, "pool": pool, "descs": descs, "base": base}
+
+
+def batch_desc_for(tb, b, i):
+    """Descriptor array read by iteration i: replica (i mod K_b), via the library's rotation."""
+    (addr,) = tb.tb_rotate_sources([b["base"]], b["stride"], b["kb"], i)
+    return b["descs"][addr]
+
+
+# ---------------------------------------------------------------------------
+# the benchmark step
+# ---------------------------------------------------------------------------
+
+def main_line(args, torch, tb, wl):
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    w = wl.REDUCE_CONFIGS["c2_reduce2_256MiB_rot"]
+    rs, dst = setup_reduce(torch, w)
+    batch = wl.batch_c4()
+    b = setup_batch(torch, tb, batch, wl.DEFAULT_ROTATE_BYTES)
+    dst_ptr = int(dst.data_ptr())
+
+    def rc(i):
+        ptrs = rs.pointers(i)                      # rotation: before the launch, untimed work
+        return lambda: tb.tb_reduce_copy(dst_ptr, ptrs, w.nfloats, sh)
+
+    def bc(i):
+        d = batch_desc_for(tb, b, i)
+        return lambda: tb.tb_batched_copy(int(d.data_ptr()), batch.ncopies, sh)
+
+    for i in range(-args.warmup, 0):
+        rc(i)()
+        bc(i)()
+    torch.cuda.synchronize()
+
+    launches = []
+    for i in range(args.steps):
+        launches += [rc(i), bc(i)]
+    ms, total_ms, wall = Timed(torch, tb, stream).run(launches)
+    rc_ms, bc_ms = ms[0::2], ms[1::2]
+
+    rc_bytes, bc_bytes = w.algorithmic_bytes, batch.algorithmic_bytes
+    step_bytes = rc_bytes + bc_bytes
+    value = args.steps * step_bytes / (total_ms * 1e-3) / 1e9
+    rc_mean, bc_mean = statistics.mean(rc_ms), statistics.mean(bc_ms)
+    rc_gbps = rc_bytes / (rc_mean * 1e-3) / 1e9
+    bc_gbps = bc_bytes / (bc_mean * 1e-3) / 1e9
+    info = tb.tb_launch_info(w.nfloats, w.nsrc)
+    traffic = _traffic("reduce_copy")
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "rotated 2-source fp32 reduce-copy, 256 MiB per buffer (67,108,864 floats, "
+                        "PrepSrcValue sources, SRC_ROTATE_BYTES=256 MiB -> K=1) + batched scattered copy "
+                        "of 47,520 copies log-uniform 64 B-16 KiB into random 16 KiB slots of a 4 GiB pool "
+                        f"(K_b={b['kb']} source replicas), one of each per step",
+            "reduce_copy": {"nsrc": w.nsrc, "nfloats": w.nfloats, "rotate_bytes": w.rotate_bytes, "k": rs.k,
+                            "bytes_per_launch": rc_bytes},
+            "batched_copy": {"ncopies": batch.ncopies, "payload_bytes": batch.total_bytes,
+                             "bytes_per_launch": bc_bytes, "replicas": b["kb"]},
+            "launch": info,
+        },
+        "parts": {
+            "reduce_copy": {"ms_mean": round(rc_mean, 5), "ms_min": round(min(rc_ms), 5),
+                            "ms_max": round(max(rc_ms), 5), "gbps": round(rc_gbps, 1),
+                            "frac_of_peak": round(rc_gbps / HBM_PEAK_GBPS, 4)},
+            "batched_copy": {"ms_mean": round(bc_mean, 5), "ms_min": round(min(bc_ms), 5),
+                             "ms_max": round(max(bc_ms), 5), "gbps": round(bc_gbps, 1),
+                             "frac_of_peak": round(bc_gbps / HBM_PEAK_GBPS, 4),
+                             "copies_per_s": round(batch.ncopies / (bc_mean * 1e-3), 1)},
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "reduce_copy",
+            "achieved": round(rc_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(rc_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+        },
+        "wall_s_timed_region": round(wall, 4),
+    }
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"], line["validated"] = cpu_baseline(torch, w, batch, dst, b["pool"])
+    print(json.dumps(line), flush=True)
+    return line
+
+
+def cpu_baseline(torch, w, batch, dst, pool):
+    """The oracle, as it stands, timed on one host core over one full step
+    (median of 3); also checks the GPU results of the timed run against it."""
+    import numpy as np
+
+    import oracle
+    import workloads as wl
+    srcs = [oracle.gen_source(w.nfloats, b, w.fill) for b in range(w.nsrc)]
+    t_rc, exp = [], None
+    for _ in range(3):
+        t, exp = oracle.time_ref_reduce(srcs)
+        t_rc.append(t)
+    image = np.full(batch.pool_bytes, wl.POOL_FILL, dtype=np.uint8)
+    t_bc = [oracle.time_ref_batch(image, batch.payload, batch.desc) for _ in range(3)]
+    rc_s, bc_s = statistics.median(t_rc), statistics.median(t_bc)
+    step_bytes = w.algorithmic_bytes + batch.algorithmic_bytes
+    validated = {
+        "reduce_copy": oracle.first_mismatch(dst.cpu().numpy(), exp) == -1,
+        "batched_copy": oracle.first_mismatch(pool.cpu().numpy(), image) == -1,
+    }
+    cpu = {
+        "value": round(step_bytes / (rc_s + bc_s) / 1e9, 3),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "one full step on one core, median of 3: the 2-source fp32 reduce over 67,108,864 floats "
+                  "and the 47,520 descriptor memcpys into a 4 GiB host pool image",
+        "reduce_copy_gbps": round(w.algorithmic_bytes / rc_s / 1e9, 3),
+        "batched_copy_gbps": round(batch.algorithmic_bytes / bc_s / 1e9, 3),
+        "batched_copies_per_s": round(batch.ncopies / bc_s, 1),
+        "host_cores_total": os.cpu_count(),
+        "cpu_model": _cpu_model(),
+    }
+    return cpu, validated
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+# ---------------------------------------------------------------------------
+# --suite: every configuration, one JSON line each
+# ---------------------------------------------------------------------------
+
+def suite(args, torch, tb, wl):
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    timer = Timed(torch, tb, stream)
+
+    def reduce_line(w, reps=1):
+        rs, dst = setup_reduce(torch, w)
+        dptr = int(dst.data_ptr())
+        means = []
+        for _ in range(reps):
+            for i in range(-args.warmup, 0):
+                tb.tb_reduce_copy(dptr, rs.pointers(i), w.nfloats, sh)
+            launches = []
+            for i in range(args.steps):
+                ptrs = rs.pointers(i)
+                launches.append(lambda p=ptrs: tb.tb_reduce_copy(dptr, p, w.nfloats, sh))
+            ms, total, _ = timer.run(launches)
+            means.append((statistics.mean(ms), min(ms), max(ms), total))
+        med = sorted(means)[len(means) // 2]
+        gbps = w.algorithmic_bytes / (med[0] * 1e-3) / 1e9
+        out = {"config": w.name, "nsrc": w.nsrc, "nfloats": w.nfloats, "k": rs.k, "reps": reps,
+               "ms_mean": round(med[0], 5), "ms_min": round(med[1], 5), "ms_max": round(med[2], 5),
+               "gbps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+               "aggregate_gbps": round(args.steps * w.algorithmic_bytes / (med[3] * 1e-3) / 1e9, 1)}
+        del rs, dst
+        torch.cuda.empty_cache()
+        return out
+
+    def batch_line(batch, rotate_bytes, tag):
+        b = setup_batch(torch, tb, batch, rotate_bytes)
+        for i in range(-args.warmup, 0):
+            d = batch_desc_for(tb, b, i)
+            tb.tb_batched_copy(int(d.data_ptr()), batch.ncopies, sh)
+        launches = []
+        for i in range(args.steps):
+            d = batch_desc_for(tb, b, i)
+            launches.append(lambda d=d: tb.tb_batched_copy(int(d.data_ptr()), batch.ncopies, sh))
+        ms, total, _ = timer.run(launches)
+        mean = statistics.mean(ms)
+        gbps = batch.algorithmic_bytes / (mean * 1e-3) / 1e9
+        out = {"config": f"{batch.name}_{tag}", "ncopies": batch.ncopies, "payload_bytes": batch.total_bytes,
+               "replicas": b["kb"], "ms_mean": round(mean, 5), "ms_min": round(min(ms), 5),
+               "ms_max": round(max(ms), 5), "gbps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+               "copies_per_s": round(batch.ncopies / (mean * 1e-3), 1)}
+        del b
+        torch.cuda.empty_cache()
+        return out
+
+    for name in ("c1_copy_4MiB_rot", "c2_reduce2_256MiB_rot", "c2_reduce2_256MiB_norot",
+                 "c3_reduce4_64MiB_compress"):
+        print(json.dumps({"suite": reduce_line(wl.REDUCE_CONFIGS[name])}), flush=True)
+    c4 = wl.batch_c4()
+    print(json.dumps({"suite": batch_line(c4, wl.DEFAULT_ROTATE_BYTES, "rotated")}), flush=True)
+    print(json.dumps({"suite": batch_line(c4, 0, "control")}), flush=True)
+    del c4
+    c5 = wl.batch_c5()
+    print(json.dumps({"suite": batch_line(c5, wl.DEFAULT_ROTATE_BYTES, "rotated")}), flush=True)
+    del c5
+    for nbytes in wl.SWEEP_BYTES:
+        for rot in (True, False):
+            print(json.dumps({"suite": reduce_line(wl.sweep_workload(nbytes, rot), reps=3)}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--suite", action="store_true", help="also time every configuration (C1-C5, sweep)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): "
+              "this build measures the single-GPU hot path; see DESIGN.md for how it would shard.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be >= 1 and --warmup >= 0")
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU: the HIP path has no CPU fallback", file=sys.stderr, flush=True)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    import copy_reduce_amd as tb
+    import workloads as wl
+
+    if args.suite:
+        suite(args, torch, tb, wl)
+        torch.cuda.empty_cache()
+    main_line(args, torch, tb, wl)
+
+
+if __name__ == "__main__":
+    main()

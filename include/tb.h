@@ -1,0 +1,223 @@
+/*
+ * tb.h -- C ABI of libtb, the MI355X (gfx950) transfer hot path.
+ *
+ * Two operations run on the GPU:
+ *   - a multi-source fp32 reduce-copy, dst = src0 + src1 + ... + srcN-1 in a
+ *     fixed left-to-right order (a copy for N = 1, a memset for N = 0), read
+ *     through rotated source slices so that repeated launches cannot be served
+ *     from cache;
+ *   - a batched copy that runs a whole (src, dst, bytes) descriptor array in
+ *     one launch.
+ *
+ * Conventions for every entry point:
+ *   - Calls return a tb_status and never throw; the library prints nothing.
+ *   - "device pointer" means memory of the current HIP device (hipMalloc or a
+ *     torch CUDA tensor); "host pointer" means ordinary process memory.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the legacy default
+ *     stream.  GPU work is only enqueued: no call below synchronises unless it
+ *     says so, and the library never touches a stream it was not given.
+ *   - The caller owns every buffer it passes.  The library owns only the
+ *     batched-copy scratch and the spin-gate flag (freed by tb_shutdown).
+ *   - TB_ERR_HIP means a HIP runtime call failed; tb_last_hip_error() gives
+ *     its text.  Faults inside a kernel surface at the caller's next
+ *     synchronisation, as for any HIP kernel.
+ *   - There is no fallback path: if a kernel cannot be launched the call fails.
+ */
+#ifndef TB_H
+#define TB_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tb_status {
+    TB_OK = 0,
+    TB_ERR_INVALID = -1,   /* bad argument; nothing was enqueued          */
+    TB_ERR_HIP = -2,       /* a HIP runtime call failed                   */
+    TB_ERR_NOMEM = -3,     /* library scratch could not be allocated      */
+    TB_ERR_TIMEOUT = -4    /* the spin gate gave up before it was released */
+} tb_status;
+
+/* Most sources one reduce-copy takes. */
+#define TB_MAX_SRCS 16
+
+/*
+ * One copy of a batch, Mooncake RFC #5041 "HipTransport", Design of #5040:
+ * a launch runs an array of (src, dst, len) descriptors.  src and dst are
+ * device addresses, bytes the length; 24 bytes, 8-byte aligned.
+ */
+typedef struct tb_copy_desc {
+    uint64_t src;
+    uint64_t dst;
+    uint64_t bytes;
+} tb_copy_desc;
+
+/* Source pattern kinds, "TransferBench data validation", Expected source pattern. */
+enum {
+    TB_FILL_DEFAULT = 0,   /* PrepSrcValue closed form                         */
+    TB_FILL_PATTERN = 1,   /* fillPattern: a float vector repeated             */
+    TB_FILL_COMPRESS = 2   /* fillCompress: random floats, per-line zeroing mix */
+};
+
+typedef struct tb_fill_cfg {
+    int32_t kind;               /* TB_FILL_*                                       */
+    uint32_t compress_pct[5];   /* % of 64-byte lines: random, 1B0, 2B0, 4B0, 32B0 */
+    const float *pattern;       /* host array for TB_FILL_PATTERN                  */
+    uint64_t pattern_len;       /* its length in floats, > 0                       */
+    uint64_t seed;              /* TB_FILL_COMPRESS seed                           */
+} tb_fill_cfg;
+
+/* ------------------------------------------------------------------------ */
+/* Host-only calls (no GPU needed)                                           */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Number of identical source slices K for a transfer of num_bytes with
+ * SRC_ROTATE_BYTES = rotate_bytes: K = ceil(rotate_bytes / num_bytes), and 1
+ * when rotate_bytes is 0 (rotation off) or num_bytes is 0.
+ * TransferBench PR #365 "Fix one-sided remote-read bandwidth inflation via
+ * source-slice rotation (SRC_ROTATE_BYTES)", Technical Details.
+ * Errors: TB_ERR_INVALID if k_out is NULL.
+ */
+int tb_num_slices(uint64_t num_bytes, uint64_t rotate_bytes, uint64_t *k_out);
+
+/*
+ * Byte distance between consecutive slices of one source: num_bytes rounded up
+ * to a multiple of 256, so every slice starts aligned for 16-byte vector loads
+ * (PR #365 review, "Align replicated source slices for vector loads").  A
+ * source with K slices needs K * stride bytes.
+ * Errors: TB_ERR_INVALID if stride_out is NULL or the rounding overflows.
+ */
+int tb_slice_stride(uint64_t num_bytes, uint64_t *stride_out);
+
+/*
+ * PrepareReference: fill host_out[0 .. nfloats) with the reference data of
+ * source buffer buffer_idx ("TransferBench data validation", Expected source
+ * pattern).  cfg may be NULL for the default pattern
+ *   PrepSrcValue(b, i) = (((i % 383) * 517) % 383 + 31) * (b + 1)
+ * evaluated on the integer index i.  TB_FILL_PATTERN repeats cfg->pattern.
+ * TB_FILL_COMPRESS draws, per 64-byte line, a category (random, 1B0, 2B0, 4B0,
+ * 32B0) by cfg->compress_pct; each float is a multiple of 2^-23 in [-1, 1)
+ * from a SplitMix64 stream, and category nB0 zeroes the line's leading n bytes.
+ * host_out: host memory of nfloats floats, written only.
+ * Errors: TB_ERR_INVALID for NULL host_out with nfloats > 0, buffer_idx < 0,
+ * an unknown kind, an empty pattern, or percentages not summing to 100.
+ */
+int tb_prep_reference(float *host_out, uint64_t nfloats, int32_t buffer_idx,
+                      const tb_fill_cfg *cfg);
+
+/*
+ * Source-slice rotation for one iteration (PR #365, Technical Details:
+ * RotateSourceSlices; iteration i reads slice i mod K, folded into [0, K) so
+ * that negative warmup indices work):
+ *   out[b] = base[b] + ((iteration mod k + k) mod k) * slice_stride_bytes.
+ * base and out: host arrays of nsrc device addresses (out may equal base).
+ * Pure host arithmetic, meant to run outside any timed region.
+ * Errors: TB_ERR_INVALID for NULL arrays with nsrc > 0, nsrc outside
+ * [0, TB_MAX_SRCS], k == 0, or an address that would overflow.
+ */
+int tb_rotate_sources(const float *const *base, int32_t nsrc,
+                      uint64_t slice_stride_bytes, uint64_t k, int64_t iteration,
+                      const float **out);
+
+/* Text for a tb_status value (static storage). */
+const char *tb_status_string(int status);
+
+/* Text of the last failing HIP call on this thread, or "" (thread-local). */
+const char *tb_last_hip_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* GPU calls                                                                 */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Initialise the K slices of one source (PR #365, Technical Details, "Prep
+ * fill"): copy host_ref (nfloats floats, host memory) into slice 0 of dev_base,
+ * then replicate slice 0 device-to-device into slices 1 .. K-1, so the
+ * host-to-device traffic stays at one slice.  dev_base must hold
+ * k * slice_stride_bytes bytes.  Enqueued on `stream`; host_ref must stay
+ * valid until the stream has passed the copy (pageable memory is copied
+ * before the call returns).
+ * Errors: TB_ERR_INVALID for NULL pointers with nfloats > 0, k == 0,
+ * slice_stride_bytes < 4 * nfloats, or size overflow; TB_ERR_HIP.
+ */
+int tb_prep_sources(float *dev_base, uint64_t slice_stride_bytes, uint64_t k,
+                    const float *host_ref, uint64_t nfloats, void *stream);
+
+/*
+ * Reduce-copy ("TransferBench data validation", expected-value table and
+ * Expected destination): for every j < nfloats
+ *   nsrc == 0: dst bytes set to 0x00;
+ *   nsrc == 1: dst[j] = srcs[0][j], a bitwise copy;
+ *   nsrc >= 2: dst[j] = (...((srcs[0][j] + srcs[1][j]) + srcs[2][j]) ...)
+ *              + srcs[nsrc-1][j], binary32 additions rounded to nearest-even,
+ *              in exactly this order (subnormals kept).
+ * dst: device pointer to nfloats floats; srcs: HOST array of nsrc device
+ * pointers (read during the call only).  All pointers 4-byte aligned; the
+ * fast path needs every pointer to share its address modulo 16 with dst.
+ * dst may be exactly equal to a source; any other overlap between dst and a
+ * source is rejected.  Enqueues one kernel on `stream`.  nfloats == 0 is a
+ * no-op.
+ * Errors: TB_ERR_INVALID for NULL pointers with nfloats > 0, nsrc outside
+ * [0, TB_MAX_SRCS], misaligned pointers, partial overlap, or size overflow;
+ * TB_ERR_HIP if the launch failed.
+ */
+int tb_reduce_copy(float *dst, const float *const *srcs, int32_t nsrc,
+                   uint64_t nfloats, void *stream);
+
+/* As tb_reduce_copy, with the byte written for nsrc == 0 given explicitly
+ * (the MEMSET_CHAR of dstReference[0]); memset_byte must be <= 255. */
+int tb_reduce_copy_ex(float *dst, const float *const *srcs, int32_t nsrc,
+                      uint64_t nfloats, uint32_t memset_byte, void *stream);
+
+/*
+ * Batched copy (Mooncake RFC #5041, Design of #5040): for every descriptor d
+ * of desc_dev[0 .. ncopies), copy d.bytes bytes from d.src to d.dst, all in one
+ * kernel launch.  desc_dev is a DEVICE array that must stay valid and
+ * unchanged until the stream has passed the kernel.  Any alignment and any
+ * length work (16-byte vectors are used where src and dst agree modulo 16);
+ * zero-length descriptors are skipped; ncopies == 0 is a no-op.
+ * Destinations must be pairwise disjoint and disjoint from every source;
+ * overlapping descriptors give unspecified bytes in the overlap (not checked:
+ * the descriptors are in device memory).
+ * The kernel uses a small library-owned scratch area per (device, stream),
+ * allocated on the first call for that pair; calls on one stream are ordered,
+ * calls on different streams use different scratch.
+ * Errors: TB_ERR_INVALID for a NULL or misaligned desc_dev with ncopies > 0;
+ * TB_ERR_NOMEM if the scratch cannot be allocated; TB_ERR_HIP.
+ */
+int tb_batched_copy(const tb_copy_desc *desc_dev, uint32_t ncopies, void *stream);
+
+/*
+ * Timing gate (nvbandwidth's spin kernel, "nvbandwidth deep dive" §3.3.1):
+ * tb_spin_gate_arm enqueues on `stream` a one-thread kernel that waits until
+ * tb_spin_gate_release() is called, so that work queued behind it starts back
+ * to back once released.  The wait is bounded: after timeout_ms (1 .. 60000)
+ * the kernel exits by itself and tb_spin_gate_status() then returns
+ * TB_ERR_TIMEOUT.  One gate per process; arming again re-uses it.
+ * tb_spin_gate_status must be called after the stream has been synchronised.
+ */
+int tb_spin_gate_arm(uint32_t timeout_ms, void *stream);
+int tb_spin_gate_release(void);
+int tb_spin_gate_status(void);
+
+/*
+ * Launch geometry the library uses on the current device: compute units and
+ * the workgroup counts of the reduce-copy and batched-copy kernels for the
+ * given sizes (for reports; no GPU work is enqueued).  Any out pointer may be
+ * NULL.  Errors: TB_ERR_HIP if the device cannot be queried.
+ */
+int tb_launch_info(uint64_t nfloats, int32_t nsrc, int32_t *cu_count,
+                   int32_t *reduce_blocks, int32_t *batched_blocks);
+
+/* Free the library's scratch and gate memory (waits for the device first).
+ * Safe to call more than once; later calls re-allocate lazily. */
+int tb_shutdown(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TB_H */

@@ -1,0 +1,207 @@
+"""GPU parity of the reduce-copy (tb_reduce_copy through the C ABI) against the
+oracle: bit-exact, every N from 0 to 16, ragged sizes, independent pointer
+offsets, in-place alias, special values, rotation selection, source prep."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from gpu_util import DevBuf, note, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+SIZES = [0, 1, 3, 4, 5, 63, 64, 65, 1023, 1025, 4096 * 3 + 7, (1 << 20) + 7]
+
+
+def _sources(nsrc, n, kind="compress", seed=3):
+    if kind == "compress":
+        return [oracle.gen_compress(n, b, wl.C3_PCT, seed) for b in range(nsrc)]
+    return [oracle.gen_default(n, b) for b in range(nsrc)]
+
+
+def _run(torch, srcs, n, dst_off=0, src_offs=None, memset_byte=0, prefill=0xFF):
+    import copy_reduce_amd as tb
+    nsrc = len(srcs)
+    src_offs = src_offs or [0] * nsrc
+    sbufs = [DevBuf(torch, n * 4, o).upload(s[:n]) for s, o in zip(srcs, src_offs)]
+    dbuf = DevBuf(torch, n * 4, dst_off, fill=prefill)
+    stream = torch.cuda.current_stream().cuda_stream
+    tb.tb_reduce_copy(dbuf.ptr, [b.ptr for b in sbufs], n, stream, memset_byte)
+    torch.cuda.synchronize()
+    got = dbuf.download().view(np.float32) if n else np.zeros(0, np.float32)
+    exp = oracle.ref_reduce([s[:n] for s in srcs], n=n, memset_byte=memset_byte)
+    return got, exp, dbuf, sbufs
+
+
+@pytest.mark.parametrize("nsrc", list(range(0, 17)))
+@pytest.mark.parametrize("n", SIZES)
+def test_reduce_copy_all_n_ragged(nsrc, n):
+    torch = require_gpu()
+    note(f"reduce_copy nsrc={nsrc} n={n} compress seed=3")
+    srcs = _sources(nsrc, n)
+    got, exp, dbuf, _ = _run(torch, srcs, n)
+    assert oracle.first_mismatch(got, exp) == -1
+    assert dbuf.guards_intact()
+
+
+@pytest.mark.parametrize("offs", [(d, s0, s1) for d in (0, 4, 8, 12) for s0 in (0, 4, 8, 12) for s1 in (0, 4, 8, 12)])
+def test_reduce_copy_pointer_offsets_n2(offs):
+    torch = require_gpu()
+    n = 4096 + 13
+    note(f"reduce_copy nsrc=2 n={n} offsets={offs}")
+    got, exp, dbuf, _ = _run(torch, _sources(2, n), n, dst_off=offs[0], src_offs=list(offs[1:]))
+    assert oracle.first_mismatch(got, exp) == -1
+    assert dbuf.guards_intact()
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_reduce_copy_pointer_offsets_random(seed):
+    torch = require_gpu()
+    rng = np.random.default_rng(seed)
+    nsrc = int(rng.integers(1, 17))
+    n = int(rng.integers(1, 70000))
+    offs = [int(x) * 4 for x in rng.integers(0, 4, size=nsrc + 1)]
+    note(f"reduce_copy nsrc={nsrc} n={n} offsets={offs}")
+    got, exp, dbuf, _ = _run(torch, _sources(nsrc, n, seed=seed), n, dst_off=offs[0], src_offs=offs[1:])
+    assert oracle.first_mismatch(got, exp) == -1
+    assert dbuf.guards_intact()
+
+
+@pytest.mark.parametrize("nsrc", [1, 2, 4])
+def test_reduce_copy_default_pattern_large(nsrc):
+    torch = require_gpu()
+    n = (1 << 22) + 3
+    note(f"reduce_copy nsrc={nsrc} n={n} default pattern")
+    got, exp, _, _ = _run(torch, _sources(nsrc, n, "default"), n)
+    assert oracle.first_mismatch(got, exp) == -1
+
+
+@pytest.mark.parametrize("mb", [0x00, 0x5A, 0xFF])
+def test_reduce_copy_memset_byte(mb):
+    torch = require_gpu()
+    n = 100003
+    note(f"reduce_copy nsrc=0 n={n} memset={mb:#x}")
+    got, exp, dbuf, _ = _run(torch, [], n, dst_off=4, memset_byte=mb, prefill=0x11)
+    assert oracle.first_mismatch(got, exp) == -1 and dbuf.guards_intact()
+
+
+@pytest.mark.parametrize("nsrc", [1, 2, 3, 16])
+def test_reduce_copy_in_place_alias(nsrc):
+    """dst == src0 exactly: every element is read before it is written."""
+    import copy_reduce_amd as tb
+    torch = require_gpu()
+    n = 300001
+    note(f"reduce_copy in-place nsrc={nsrc} n={n}")
+    srcs = _sources(nsrc, n, seed=5)
+    bufs = [DevBuf(torch, n * 4).upload(s) for s in srcs]
+    tb.tb_reduce_copy(bufs[0].ptr, [b.ptr for b in bufs], n, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert oracle.first_mismatch(bufs[0].download().view(np.float32), oracle.ref_reduce(srcs)) == -1
+
+
+def test_reduce_copy_special_values():
+    torch = require_gpu()
+    n = 4096
+    rng = np.random.default_rng(7)
+    raw = rng.integers(0, 2**32, size=n, dtype=np.uint64).astype(np.uint32)
+    specials = np.array([0x80000000, 0x00000000, 0x00000001, 0x807FFFFF, 0x00400000, 0x7F800000,
+                         0xFF800000, 0x7F7FFFFF, 0xFF7FFFFF, 0x7FC00001, 0xFFC12345, 0x7F800001], dtype=np.uint32)
+    raw[:specials.size] = specials
+    raw[2048:2048 + specials.size] = specials
+    a = raw.view(np.float32)
+    # N = 1 is a bitwise copy, NaN payloads included
+    note("reduce_copy nsrc=1 special values incl. NaN payloads")
+    got, exp, _, _ = _run(torch, [a], n)
+    assert np.array_equal(got.view(np.uint32), raw)
+    # N >= 2 over signed zeros, subnormals, infinities, extremes (no NaN: payloads are not part of the contract)
+    finite = np.where(np.isnan(a), np.float32(0.5), a).astype(np.float32)
+    b = np.roll(finite, 5)
+    c = -np.roll(finite, 11)
+    note("reduce_copy nsrc=2,3 special values without NaN")
+    for srcs in ([finite, b], [finite, b, c], [c, finite, b]):
+        got, exp, _, _ = _run(torch, srcs, n)
+        nan_both = np.isnan(got) & np.isnan(exp)
+        assert np.array_equal(got.view(np.uint32)[~nan_both], exp.view(np.uint32)[~nan_both])
+
+
+def test_reduce_copy_fixed_order_worked_examples():
+    from conftest import read_golden
+    torch = require_gpu()
+    for row in read_golden("fp32_order_cases.txt"):
+        exp_hex, srcs = row.split(";")
+        srcs = [np.full(77, np.uint32(int(h, 16)), dtype=np.uint32).view(np.float32) for h in srcs.split()]
+        note(f"reduce_copy worked example {row}")
+        got, exp, _, _ = _run(torch, srcs, 77)
+        assert np.all(got.view(np.uint32) == np.uint32(int(exp_hex, 16))), row
+
+
+def test_prep_sources_replicates_slices():
+    """validateSource: after prep every slice equals the host reference."""
+    from copy_reduce_amd.torch_api import RotatedSources
+    torch = require_gpu()
+    for nfloats, rot in [(1 << 20, 256 << 20), (1000, 1 << 20), (12345, 100000), (4096, 0)]:
+        note(f"prep_sources nfloats={nfloats} R={rot}")
+        rs = RotatedSources(2, nfloats, rot, fill=("compress", wl.C3_PCT, 3))
+        torch.cuda.synchronize()
+        assert rs.k == oracle.num_slices(nfloats * 4, rot)
+        for b in range(2):
+            ref = oracle.gen_compress(nfloats, b, wl.C3_PCT, 3)
+            for s in range(rs.k):
+                got = rs.slice_view(b, s).cpu().numpy()
+                assert oracle.first_mismatch(got, ref) == -1, (b, s)
+
+
+def test_rotation_selects_slice_i_mod_k():
+    """Every slice holds the same data in real runs, so validation cannot see a
+    rotation bug; here slice s of source b holds PrepSrcValue(s + 16 b, .) instead
+    and launch i must return exactly slice ((i mod K) + K) mod K."""
+    import copy_reduce_amd as tb
+    torch = require_gpu()
+    nfloats, rot, nsrc = 4096 + 3, 16 * 4096 * 4, 2
+    k = tb.tb_num_slices(nfloats * 4, rot)
+    stride = tb.tb_slice_stride(nfloats * 4)
+    assert k == 16
+    bufs = [torch.empty(k * stride, dtype=torch.uint8, device="cuda") for _ in range(nsrc)]
+    for b in range(nsrc):
+        for s in range(k):
+            data = oracle.gen_default(nfloats, s + 16 * b)
+            bufs[b][s * stride:s * stride + nfloats * 4].copy_(torch.from_numpy(data.view(np.uint8).copy()))
+    dst = torch.empty(nfloats, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    for i in range(-3, 2 * k + 1):
+        note(f"rotation iteration {i} k={k}")
+        ptrs = tb.tb_rotate_sources([int(t.data_ptr()) for t in bufs], stride, k, i)
+        tb.tb_reduce_copy(int(dst.data_ptr()), ptrs, nfloats, stream)
+        torch.cuda.synchronize()
+        s = oracle.slice_of(i, k)
+        exp = oracle.ref_reduce([oracle.gen_default(nfloats, s + 16 * b) for b in range(nsrc)])
+        assert oracle.first_mismatch(dst.cpu().numpy(), exp) == -1, i
+
+
+def test_reduce_copy_on_side_stream():
+    import copy_reduce_amd as tb
+    torch = require_gpu()
+    n = 1 << 18
+    srcs = _sources(3, n, seed=11)
+    bufs = [DevBuf(torch, n * 4).upload(s) for s in srcs]
+    dst = DevBuf(torch, n * 4)
+    side = torch.cuda.Stream()
+    note("reduce_copy on a side stream")
+    torch.cuda.synchronize()
+    tb.tb_reduce_copy(dst.ptr, [b.ptr for b in bufs], n, side.cuda_stream)
+    side.synchronize()
+    assert oracle.first_mismatch(dst.download().view(np.float32), oracle.ref_reduce(srcs)) == -1
+
+
+def test_reduce_copy_invalid_args_enqueue_nothing():
+    import copy_reduce_amd as tb
+    torch = require_gpu()
+    n = 1024
+    dst = DevBuf(torch, n * 4, fill=0x33)
+    src = DevBuf(torch, n * 4).upload(oracle.gen_default(n, 0))
+    arr = (ctypes.c_void_p * 1)(src.ptr + 2)
+    assert tb.lib.tb_reduce_copy(dst.ptr, arr, 1, n, None) == tb.TB_ERR_INVALID
+    torch.cuda.synchronize()
+    assert np.all(dst.download() == 0x33)
