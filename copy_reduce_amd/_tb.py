@@ -26,6 +26,12 @@ EXPORTS = (
     "tb_spin_gate_status", "tb_launch_info", "tb_shutdown",
 )
 
+# torch ships its own HIP runtime under the same soname (libamdhip64.so.7) as
+# /opt/rocm's.  Loading torch first makes libtb bind to that one runtime;
+# loading libtb first would bring up a second runtime that sees no device
+# once torch starts its own.
+import torch  # noqa: E402,F401
+
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"{LIB_PATH} is missing: build the HIP library first "
