@@ -322,6 +322,19 @@ def suite(args, torch, tb, wl):
             print(json.dumps({"suite": reduce_line(wl.sweep_workload(nbytes, rot), reps=3)}), flush=True)
 
 
+def calibrate_copy(torch, tb):
+    """A plain copy of exactly 268,435,456 bytes read and 268,435,456 written per launch."""
+    nbytes = 256 << 20
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    sh = torch.cuda.current_stream().cuda_stream
+    for _ in range(10):
+        tb.tb_reduce_copy(int(dst.data_ptr()), [int(src.data_ptr())], nbytes // 4, sh)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "tb_reduce_copy nsrc=1", "bytes_read_per_launch": nbytes,
+                      "bytes_written_per_launch": nbytes, "launches": 10}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -329,6 +342,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--suite", action="store_true", help="also time every configuration (C1-C5, sweep)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 256 MiB copy (tb_reduce_copy, one source) 10 times: the known-size "
+                         "kernel that scales rocprofv3's FETCH_SIZE / WRITE_SIZE into HBM bytes")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -348,6 +364,9 @@ def main():
     import copy_reduce_amd as tb
     import workloads as wl
 
+    if args.calibrate_copy:
+        calibrate_copy(torch, tb)
+        return
     if args.suite:
         suite(args, torch, tb, wl)
         torch.cuda.empty_cache()

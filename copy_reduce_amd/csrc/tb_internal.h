@@ -13,8 +13,9 @@ namespace tbk {
 
 // Workgroup size of the reduce-copy kernels (4 wave64s).
 constexpr int kRcBlock = 256;
-// Resident workgroups aimed for per compute unit (8 x 4 waves = 32 waves/CU).
-constexpr int kRcBlocksPerCu = 8;
+// Grid cap of the reduce-copy (a multiple of 8); below it every tile has its
+// own workgroup.
+constexpr uint64_t kRcMaxBlocks = 1u << 20;
 
 struct ReduceArgs {
     float *dst;
@@ -39,7 +40,7 @@ hipError_t launch_reduce_copy(const ReduceArgs &args, int nsrc, bool vector_path
 // ---- batched copy ------------------------------------------------------------
 
 constexpr int kBcBlock = 256;        // 4 wave64s per workgroup
-constexpr int kBcBlocksPerCu = 8;    // persistent grid: 32 waves per CU
+constexpr int kBcBlocksPerCu = 8;    // persistent grid: 32 waves per CU; grid = CUs x 8
 // Copies longer than this are split into kBcChunk pieces shared by all waves.
 constexpr uint64_t kBcSplitAbove = 64 * 1024;
 constexpr uint64_t kBcChunk = 32 * 1024;
@@ -51,10 +52,16 @@ struct BcSlot {
     uint32_t next_chunk;   // next unclaimed chunk
 };
 
+struct alignas(256) BcCounter {
+    uint32_t count;
+    uint32_t pad[63];
+};
+
 struct BcScratch {
     uint32_t qtail;        // slots handed out (may exceed kBcQueueCap)
-    uint32_t done;         // workgroups finished
-    uint32_t pad[62];      // keep the counters on their own 256 bytes
+    uint32_t done_all;     // XCD groups finished
+    uint32_t pad[62];      // keep these counters on their own 256 bytes
+    BcCounter done_xcd[8]; // workgroups finished, per XCD (blockIdx % 8)
     BcSlot slot[kBcQueueCap];
 };
 

@@ -20,66 +20,116 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 //  adds the others one at a time, left to right.)
 // ============================================================================
 
-// float4s per thread per tile: enough loads in flight without spilling.
+// Global-address-space views: loads and stores become global_* instructions
+// (generic pointers would give flat_* ones, which the compiler serialises).
+typedef __attribute__((address_space(1))) f32x4 gf32x4;
+typedef __attribute__((address_space(1))) float gf32;
+typedef __attribute__((address_space(1))) u32x4 gu32x4;
+typedef __attribute__((address_space(1))) uint32_t gu32;
+typedef __attribute__((address_space(1))) uint8_t gu8;
+
+// Cache-policy bits of gfx950 buffer instructions (the aux operand): nt marks
+// the line for early eviction (streaming); sc0 / sc1 set the coherence scope
+// (sc1 = device, sc0 | sc1 = system), which makes a store write through the
+// per-XCD L2 instead of sitting there dirty until the end of the kernel.
+constexpr int kPolNt = 2;
+constexpr int kPolSc0 = 1;
+constexpr int kPolSc1 = 16;
+
+// Raw buffer resource over [base, base + bytes): accesses outside the range
+// read as zero and are not written (the hardware checks every access).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(uint64_t base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// float4s per thread per tile.  One tile per workgroup with few loads per
+// thread measured best on MI355X: the dispatcher keeps every CU full and no
+// thread holds many registers.
 template <int N>
 constexpr int rc_unroll() {
-    return N <= 2 ? 4 : (N <= 4 ? 2 : 1);
+    return N <= 2 ? 1 : (N <= 4 ? 2 : 1);
 }
 
-template <typename T>
-__device__ __forceinline__ T rc_load(const T *p) {
-    return __builtin_nontemporal_load(p);
+// Sources are streamed once per launch: nontemporal loads (without them the
+// kernel measured 73% of peak instead of 92%).  Results are written with
+// device-scope (sc1) stores, through L2 to the memory side: measured faster
+// than plain stores (lines left dirty in L2) and than nontemporal ones.
+__device__ __forceinline__ f32x4 rc_load(const gf32x4 *p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ float rc_load(const gf32 *p) { return __builtin_nontemporal_load(p); }
+
+// Workgroup b runs on XCD b % 8 (round-robin dispatch).  Give each XCD one
+// contiguous eighth of the tiles, walked in order, instead of every eighth
+// tile: measured faster on the streaming kernels.  `v` is the virtual block
+// index in [0, 8 * ceil(ntiles / 8)); returns false for the few virtual blocks
+// that have no tile.  A bijection onto [0, ntiles).
+__device__ __forceinline__ bool xcd_tile(uint64_t v, uint64_t ntiles, uint64_t *tile) {
+    const uint64_t q = ntiles >> 3, r = ntiles & 7;
+    const uint64_t x = v & 7, k = v >> 3;
+    const uint64_t count = q + (x < r ? 1 : 0);
+    if (k >= count)
+        return false;
+    *tile = x * q + (x < r ? x : r) + k;
+    return true;
 }
 
-template <typename T>
-__device__ __forceinline__ void rc_store(T *p, T v) {
-    __builtin_nontemporal_store(v, p);
-}
+__device__ __forceinline__ uint64_t virtual_blocks(uint64_t ntiles) { return (ntiles + 7) & ~(uint64_t)7; }
 
 // Fixed-order scalar sum of element j (used for the unaligned head and tail).
 template <int N>
 __device__ __forceinline__ float rc_sum_scalar(const ReduceArgs &a, uint64_t j) {
-    float acc = a.src[0][j];
+    float acc = rc_load((const gf32 *)(a.src[0]) + j);
 #pragma unroll
     for (int k = 1; k < N; k++)
-        acc = acc + a.src[k][j];
+        acc = acc + rc_load((const gf32 *)(a.src[k]) + j);
     return acc;
 }
 
 // Vector path: every pointer is congruent to dst modulo 16.  Tiles of
-// kRcBlock * U float4s are dealt to workgroups round-robin; each thread loads
-// U float4s from every source before the first addition, so N * U 16-byte
-// loads per thread are in flight.
+// kRcBlock * U float4s; each thread loads U float4s from every source before
+// the first addition, so N * U 16-byte loads per thread are in flight.
+// gridDim.x is a multiple of 8 (see reduce_grid), so the grid-stride step
+// keeps a workgroup on its XCD's share of the tiles.
 template <int N>
 __global__ __launch_bounds__(kRcBlock) void rc_vec_kernel(ReduceArgs a) {
     constexpr int U = rc_unroll<N>();
     constexpr uint64_t kTile = (uint64_t)kRcBlock * U;
     const uint64_t nvec = a.nvec;
-    f32x4 *dst = reinterpret_cast<f32x4 *>(a.dst + a.head);
-    const f32x4 *src[N];
+    const uint64_t ntiles = (nvec + kTile - 1) / kTile;
+    const gf32x4 *src[N];
 #pragma unroll
     for (int k = 0; k < N; k++)
-        src[k] = reinterpret_cast<const f32x4 *>(a.src[k] + a.head);
+        src[k] = (const gf32x4 *)(a.src[k] + a.head);
 
-    for (uint64_t base = (uint64_t)blockIdx.x * kTile; base < nvec;
-         base += (uint64_t)gridDim.x * kTile) {
+    const uint64_t vend = virtual_blocks(ntiles);
+    for (uint64_t v = blockIdx.x; v < vend; v += gridDim.x) {
+        uint64_t t;
+        if (!xcd_tile(v, ntiles, &t))
+            continue;
+        const uint64_t base = t * kTile;
         const uint64_t i0 = base + threadIdx.x;
         if (base + kTile <= nvec) {
-            f32x4 v[N][U];
+            f32x4 val[N][U];
 #pragma unroll
             for (int k = 0; k < N; k++)
 #pragma unroll
                 for (int u = 0; u < U; u++)
-                    v[k][u] = rc_load(src[k] + i0 + (uint64_t)u * kRcBlock);
+                    val[k][u] = rc_load(src[k] + i0 + (uint64_t)u * kRcBlock);
+            const __amdgpu_buffer_rsrc_t out =
+                buffer_over(reinterpret_cast<uint64_t>(a.dst + a.head) + base * 16, (uint32_t)(kTile * 16));
 #pragma unroll
             for (int u = 0; u < U; u++) {
-                f32x4 acc = v[0][u];
+                f32x4 acc = val[0][u];
 #pragma unroll
                 for (int k = 1; k < N; k++)
-                    acc = acc + v[k][u];
-                rc_store(dst + i0 + (uint64_t)u * kRcBlock, acc);
+                    acc = acc + val[k][u];
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), out, threadIdx.x * 16,
+                                                       u * kRcBlock * 16, kPolSc1);
             }
         } else {
+            // the last, partial tile: stores past nvec are dropped by the range check
+            const __amdgpu_buffer_rsrc_t out =
+                buffer_over(reinterpret_cast<uint64_t>(a.dst + a.head) + base * 16, (uint32_t)((nvec - base) * 16));
 #pragma unroll
             for (int u = 0; u < U; u++) {
                 const uint64_t i = i0 + (uint64_t)u * kRcBlock;
@@ -88,7 +138,8 @@ __global__ __launch_bounds__(kRcBlock) void rc_vec_kernel(ReduceArgs a) {
 #pragma unroll
                     for (int k = 1; k < N; k++)
                         acc = acc + rc_load(src[k] + i);
-                    rc_store(dst + i, acc);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), out,
+                                                           (threadIdx.x + u * kRcBlock) * 16, 0, kPolSc1);
                 }
             }
         }
@@ -96,12 +147,13 @@ __global__ __launch_bounds__(kRcBlock) void rc_vec_kernel(ReduceArgs a) {
 
     // Up to 3 floats before the aligned body and 3 after it.
     if (blockIdx.x == 0) {
+        gf32 *d = (gf32 *)(a.dst);
         if (threadIdx.x < a.head) {
             const uint64_t j = threadIdx.x;
-            a.dst[j] = rc_sum_scalar<N>(a, j);
+            d[j] = rc_sum_scalar<N>(a, j);
         } else if (threadIdx.x >= 64 && threadIdx.x < 64 + a.tail) {
             const uint64_t j = a.head + 4 * nvec + (threadIdx.x - 64);
-            a.dst[j] = rc_sum_scalar<N>(a, j);
+            d[j] = rc_sum_scalar<N>(a, j);
         }
     }
 }
@@ -112,26 +164,31 @@ __global__ __launch_bounds__(kRcBlock) void rc_scalar_kernel(ReduceArgs a) {
     constexpr int U = 4;
     constexpr uint64_t kTile = (uint64_t)kRcBlock * U;
     const uint64_t n = a.n;
+    gf32 *dst = (gf32 *)(a.dst);
+    const gf32 *src[N];
+#pragma unroll
+    for (int k = 0; k < N; k++)
+        src[k] = (const gf32 *)(a.src[k]);
     for (uint64_t base = (uint64_t)blockIdx.x * kTile; base < n;
          base += (uint64_t)gridDim.x * kTile) {
         const uint64_t i0 = base + threadIdx.x;
-        float v[N][U];
+        float val[N][U];
 #pragma unroll
         for (int k = 0; k < N; k++)
 #pragma unroll
             for (int u = 0; u < U; u++) {
                 const uint64_t i = i0 + (uint64_t)u * kRcBlock;
-                v[k][u] = i < n ? a.src[k][i] : 0.0f;
+                val[k][u] = i < n ? rc_load(src[k] + i) : 0.0f;
             }
 #pragma unroll
         for (int u = 0; u < U; u++) {
             const uint64_t i = i0 + (uint64_t)u * kRcBlock;
             if (i < n) {
-                float acc = v[0][u];
+                float acc = val[0][u];
 #pragma unroll
                 for (int k = 1; k < N; k++)
-                    acc = acc + v[k][u];
-                a.dst[i] = acc;
+                    acc = acc + val[k][u];
+                dst[i] = acc;
             }
         }
     }
@@ -144,18 +201,18 @@ __global__ __launch_bounds__(kRcBlock) void rc_memset_kernel(ReduceArgs a) {
     constexpr uint64_t kTile = (uint64_t)kRcBlock * U;
     const uint64_t nvec = a.nvec;
     const u32x4 fill4 = {a.fill, a.fill, a.fill, a.fill};
-    u32x4 *dst = reinterpret_cast<u32x4 *>(a.dst + a.head);
+    gu32x4 *dst = (gu32x4 *)(a.dst + a.head);
     for (uint64_t base = (uint64_t)blockIdx.x * kTile; base < nvec;
          base += (uint64_t)gridDim.x * kTile) {
 #pragma unroll
         for (int u = 0; u < U; u++) {
             const uint64_t i = base + threadIdx.x + (uint64_t)u * kRcBlock;
             if (i < nvec)
-                rc_store(dst + i, fill4);
+                dst[i] = fill4;
         }
     }
     if (blockIdx.x == 0) {
-        uint32_t *d32 = reinterpret_cast<uint32_t *>(a.dst);
+        gu32 *d32 = (gu32 *)(a.dst);
         if (threadIdx.x < a.head)
             d32[threadIdx.x] = a.fill;
         else if (threadIdx.x >= 64 && threadIdx.x < 64 + a.tail)
@@ -164,18 +221,20 @@ __global__ __launch_bounds__(kRcBlock) void rc_memset_kernel(ReduceArgs a) {
 }
 
 int reduce_grid(uint64_t nfloats, int nsrc, bool vector_path, int cu_count) {
-    uint64_t per_tile;
+    (void)cu_count;
+    uint64_t per_block;
     if (nsrc == 0)
-        per_tile = (uint64_t)kRcBlock * 4 * 4;
+        per_block = (uint64_t)kRcBlock * 4 * 4;
     else if (vector_path)
-        per_tile = (uint64_t)kRcBlock * 4 *
-                   (nsrc <= 2 ? 4 : (nsrc <= 4 ? 2 : 1));
+        per_block = (uint64_t)kRcBlock * 4 * (nsrc <= 2 ? 1 : (nsrc <= 4 ? 2 : 1));
     else
-        per_tile = (uint64_t)kRcBlock * 4;
-    uint64_t tiles = (nfloats + per_tile - 1) / per_tile;
-    uint64_t cap = (uint64_t)(cu_count > 0 ? cu_count : 1) * kRcBlocksPerCu;
-    uint64_t g = tiles < cap ? tiles : cap;
-    return (int)(g > 0 ? g : 1);
+        per_block = (uint64_t)kRcBlock * 4;
+    // one workgroup per tile, capped; the kernels loop when the cap binds
+    uint64_t g = (nfloats + per_block - 1) / per_block;
+    g = (g + 7) & ~(uint64_t)7;            // a multiple of 8: keeps the XCD map
+    if (g > kRcMaxBlocks)
+        g = kRcMaxBlocks;
+    return (int)(g > 0 ? g : 8);
 }
 
 template <int N>
@@ -245,90 +304,120 @@ __device__ __forceinline__ uint64_t readfirstlane_u64(uint64_t v) {
     return ((uint64_t)hi << 32) | lo;
 }
 
-// Copy b bytes from s to d with the whole wave; s, d, b are wave-uniform.
-__device__ __forceinline__ void wave_copy(uint64_t s, uint64_t d, uint64_t b, int lane) {
-    if (((s ^ d) & 15) == 0) {
-        // bytes up to dst's next 16-byte boundary, one per lane
-        uint64_t head = (16 - (d & 15)) & 15;
-        if (head > b)
-            head = b;
-        if ((uint64_t)lane < head)
-            reinterpret_cast<uint8_t *>(d)[lane] = reinterpret_cast<const uint8_t *>(s)[lane];
-        s += head;
-        d += head;
-        b -= head;
-        const uint64_t nv = b >> 4;
-        const u32x4 *sv = reinterpret_cast<const u32x4 *>(s);
-        u32x4 *dv = reinterpret_cast<u32x4 *>(d);
-        for (uint64_t v0 = 0; v0 < nv; v0 += 64 * kBcUnroll) {
-            u32x4 r[kBcUnroll];
+// Raw buffer load / store of one E-byte element with a cache policy.
+template <int E>
+struct BufElem;
+template <>
+struct BufElem<1> {
+    typedef uint8_t T;
+    template <int Pol>
+    static __device__ __forceinline__ T load(__amdgpu_buffer_rsrc_t r, int vo, int so) {
+        return __builtin_amdgcn_raw_buffer_load_b8(r, vo, so, Pol);
+    }
+    template <int Pol>
+    static __device__ __forceinline__ void store(T v, __amdgpu_buffer_rsrc_t r, int vo, int so) {
+        __builtin_amdgcn_raw_buffer_store_b8(v, r, vo, so, Pol);
+    }
+};
+template <>
+struct BufElem<4> {
+    typedef uint32_t T;
+    template <int Pol>
+    static __device__ __forceinline__ T load(__amdgpu_buffer_rsrc_t r, int vo, int so) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, vo, so, Pol);
+    }
+    template <int Pol>
+    static __device__ __forceinline__ void store(T v, __amdgpu_buffer_rsrc_t r, int vo, int so) {
+        __builtin_amdgcn_raw_buffer_store_b32(v, r, vo, so, Pol);
+    }
+};
+template <>
+struct BufElem<16> {
+    typedef u32x4 T;
+    template <int Pol>
+    static __device__ __forceinline__ T load(__amdgpu_buffer_rsrc_t r, int vo, int so) {
+        return __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, Pol);
+    }
+    template <int Pol>
+    static __device__ __forceinline__ void store(T v, __amdgpu_buffer_rsrc_t r, int vo, int so) {
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, vo, so, Pol);
+    }
+};
+
+// Cache policies of the batched copy.  Every source byte is read once per
+// launch: nontemporal loads.  Stores are nontemporal with system scope
+// (nt sc0 sc1): they go out to HBM without leaving scattered dirty lines in
+// the caches for the next kernel to drain.  Measured on MI355X in the bench
+// step (reduce-copy then batched copy): this beat plain and device-scope
+// stores by 15-35 us per step.
+constexpr int kBcLoadPol = kPolNt;
+constexpr int kBcStorePol = kPolNt | kPolSc0 | kPolSc1;
+
+// Copy n elements of E bytes from s to d with the whole wave (s, d, n
+// wave-uniform; s and d E-byte aligned).  Each step covers kBcUnroll slots of
+// 64 elements and issues all its loads back to back before its stores.  Every
+// slot has its own raw buffer resource over exactly the bytes it may touch
+// (possibly none), addressed by the lane offset alone: the hardware range
+// check covers the voffset (not the scalar soffset), so lanes past the end of
+// the copy read zero and their stores are dropped, and no access ever leaves
+// [s, s + n E) or [d, d + n E).  No predication, one VGPR of addressing.
+template <int E>
+__device__ __forceinline__ void wave_copy_buf(uint64_t s, uint64_t d, uint64_t n, int lane) {
+    typedef typename BufElem<E>::T T;
+    constexpr uint64_t kSlot = 64 * E;                 // bytes per slot
+    constexpr uint64_t kStepBytes = kSlot * kBcUnroll;
+    const uint64_t total = n * E;
+    for (uint64_t b0 = 0; b0 < total; b0 += kStepBytes) {
+        const uint64_t left = total - b0;
+        T r[kBcUnroll];
 #pragma unroll
-            for (int u = 0; u < kBcUnroll; u++) {
-                const uint64_t i = v0 + (uint64_t)u * 64 + lane;
-                if (i < nv)
-                    r[u] = sv[i];
-            }
-#pragma unroll
-            for (int u = 0; u < kBcUnroll; u++) {
-                const uint64_t i = v0 + (uint64_t)u * 64 + lane;
-                if (i < nv)
-                    dv[i] = r[u];
-            }
+        for (int u = 0; u < kBcUnroll; u++) {
+            const uint64_t off = (uint64_t)u * kSlot;
+            const uint32_t rec = left > off ? (uint32_t)(left - off < kSlot ? left - off : kSlot) : 0u;
+            r[u] = BufElem<E>::template load<kBcLoadPol>(buffer_over(s + b0 + off, rec), lane * E, 0);
         }
-        const uint64_t tail = b & 15;
-        if ((uint64_t)lane < tail)
-            reinterpret_cast<uint8_t *>(d)[nv * 16 + lane] =
-                reinterpret_cast<const uint8_t *>(s)[nv * 16 + lane];
-    } else if (((s ^ d) & 3) == 0) {
-        uint64_t head = (4 - (d & 3)) & 3;
-        if (head > b)
-            head = b;
-        if ((uint64_t)lane < head)
-            reinterpret_cast<uint8_t *>(d)[lane] = reinterpret_cast<const uint8_t *>(s)[lane];
-        s += head;
-        d += head;
-        b -= head;
-        const uint64_t nw = b >> 2;
-        const uint32_t *sw = reinterpret_cast<const uint32_t *>(s);
-        uint32_t *dw = reinterpret_cast<uint32_t *>(d);
-        for (uint64_t w0 = 0; w0 < nw; w0 += 64 * kBcUnroll) {
-            uint32_t r[kBcUnroll];
 #pragma unroll
-            for (int u = 0; u < kBcUnroll; u++) {
-                const uint64_t i = w0 + (uint64_t)u * 64 + lane;
-                if (i < nw)
-                    r[u] = sw[i];
-            }
-#pragma unroll
-            for (int u = 0; u < kBcUnroll; u++) {
-                const uint64_t i = w0 + (uint64_t)u * 64 + lane;
-                if (i < nw)
-                    dw[i] = r[u];
-            }
-        }
-        const uint64_t tail = b & 3;
-        if ((uint64_t)lane < tail)
-            reinterpret_cast<uint8_t *>(d)[nw * 4 + lane] =
-                reinterpret_cast<const uint8_t *>(s)[nw * 4 + lane];
-    } else {
-        const uint8_t *sb = reinterpret_cast<const uint8_t *>(s);
-        uint8_t *db = reinterpret_cast<uint8_t *>(d);
-        for (uint64_t o0 = 0; o0 < b; o0 += 64 * kBcUnroll) {
-            uint8_t r[kBcUnroll];
-#pragma unroll
-            for (int u = 0; u < kBcUnroll; u++) {
-                const uint64_t o = o0 + (uint64_t)u * 64 + lane;
-                if (o < b)
-                    r[u] = sb[o];
-            }
-#pragma unroll
-            for (int u = 0; u < kBcUnroll; u++) {
-                const uint64_t o = o0 + (uint64_t)u * 64 + lane;
-                if (o < b)
-                    db[o] = r[u];
-            }
+        for (int u = 0; u < kBcUnroll; u++) {
+            const uint64_t off = (uint64_t)u * kSlot;
+            const uint32_t rec = left > off ? (uint32_t)(left - off < kSlot ? left - off : kSlot) : 0u;
+            BufElem<E>::template store<kBcStorePol>(r[u], buffer_over(d + b0 + off, rec), lane * E, 0);
         }
     }
+}
+
+// Up to 63 single bytes, one per lane (range-checked: lanes past n do nothing).
+__device__ __forceinline__ void wave_copy_few_bytes(uint64_t s, uint64_t d, uint64_t n, int lane) {
+    if (n == 0)
+        return;
+    const __amdgpu_buffer_rsrc_t in = buffer_over(s, (uint32_t)n);
+    const __amdgpu_buffer_rsrc_t out = buffer_over(d, (uint32_t)n);
+    BufElem<1>::store<kBcStorePol>(BufElem<1>::load<kBcLoadPol>(in, lane, 0), out, lane, 0);
+}
+
+// Copy b bytes from s to d with the whole wave; s, d, b are wave-uniform.
+// 16-byte elements when s and d agree modulo 16 (bytes before dst's first
+// 16-byte boundary and after the last one go one per lane), dwords when they
+// agree modulo 4, single bytes otherwise.
+__device__ __forceinline__ void wave_copy(uint64_t s, uint64_t d, uint64_t b, int lane) {
+    const uint64_t mis = (s ^ d) & 15;
+    if (mis != 0 && (mis & 3) != 0) {
+        wave_copy_buf<1>(s, d, b, lane);
+        return;
+    }
+    const uint64_t g = mis == 0 ? 16 : 4;
+    uint64_t head = (g - (d & (g - 1))) & (g - 1);
+    if (head > b)
+        head = b;
+    wave_copy_few_bytes(s, d, head, lane);
+    s += head;
+    d += head;
+    b -= head;
+    const uint64_t body = b & ~(g - 1);
+    if (g == 16)
+        wave_copy_buf<16>(s, d, body >> 4, lane);
+    else
+        wave_copy_buf<4>(s, d, body >> 2, lane);
+    wave_copy_few_bytes(s + body, d + body, b - body, lane);
 }
 
 __device__ __forceinline__ uint32_t atomic_load_agent(const uint32_t *p) {
@@ -343,7 +432,7 @@ __device__ __forceinline__ uint32_t atomic_add_agent(uint32_t *p, uint32_t v) {
     return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__global__ __launch_bounds__(kBcBlock) void bc_kernel(const tb_copy_desc *__restrict__ desc,
+__global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_copy_desc *__restrict__ desc,
                                                       uint32_t n, BcScratch *scr) {
     const int lane = threadIdx.x & 63;
     const uint64_t W = (uint64_t)gridDim.x * (kBcBlock / 64);
@@ -408,11 +497,22 @@ __global__ __launch_bounds__(kBcBlock) void bc_kernel(const tb_copy_desc *__rest
         seen = q;
     }
 
-    // ---- the last workgroup out clears the queue for the next launch ----
+    // ---- completion: the last workgroup out clears the queue for the next
+    // launch.  Workgroups count in per-XCD counters (gridDim.x is a multiple
+    // of 8, so each XCD group has gridDim.x / 8 members); the last of each
+    // group then counts in one counter for the 8 groups.  This keeps 2,048
+    // workgroups from serialising on one address. ----
     __shared__ uint32_t last_block;
     __syncthreads();
-    if (threadIdx.x == 0)
-        last_block = (atomic_add_agent(&scr->done, 1u) == gridDim.x - 1) ? 1u : 0u;
+    if (threadIdx.x == 0) {
+        uint32_t last = 0;
+        const uint32_t x = blockIdx.x & 7;
+        if (atomic_add_agent(&scr->done_xcd[x].count, 1u) == gridDim.x / 8 - 1) {
+            atomic_store_agent(&scr->done_xcd[x].count, 0u);
+            last = atomic_add_agent(&scr->done_all, 1u) == 7 ? 1u : 0u;
+        }
+        last_block = last;
+    }
     __syncthreads();
     if (last_block) {
         uint32_t q = atomic_load_agent(&scr->qtail);
@@ -425,12 +525,13 @@ __global__ __launch_bounds__(kBcBlock) void bc_kernel(const tb_copy_desc *__rest
         __syncthreads();
         if (threadIdx.x == 0) {
             atomic_store_agent(&scr->qtail, 0u);
-            atomic_store_agent(&scr->done, 0u);
+            atomic_store_agent(&scr->done_all, 0u);
         }
     }
 }
 
 int batched_grid(int cu_count) {
+    // a multiple of 8 (the completion counters are per XCD)
     return (cu_count > 0 ? cu_count : 1) * kBcBlocksPerCu;
 }
 
