@@ -261,7 +261,8 @@ int tb_batched_copy(const tb_copy_desc *desc_dev, uint32_t ncopies, void *stream
     rc = scratch_for(s, &scratch);
     if (rc != TB_OK)
         return rc;
-    hipError_t e = tbk::launch_batched_copy(desc_dev, ncopies, scratch, info.cu_count, s);
+    const uint64_t wait_ticks = (uint64_t)tbk::kBcSealWaitUs * info.wall_clock_khz / 1000u;
+    hipError_t e = tbk::launch_batched_copy(desc_dev, ncopies, scratch, info.cu_count, wait_ticks, s);
     if (e != hipSuccess)
         return hip_fail(e, "batched-copy launch");
     return TB_OK;

@@ -40,17 +40,20 @@ hipError_t launch_reduce_copy(const ReduceArgs &args, int nsrc, bool vector_path
 // ---- batched copy ------------------------------------------------------------
 
 constexpr int kBcBlock = 256;        // 4 wave64s per workgroup
-constexpr int kBcBlocksPerCu = 8;    // persistent grid: 32 waves per CU; grid = CUs x 8
-// Copies longer than this are split into kBcChunk pieces shared by all waves.
+// Persistent grid: 7 workgroups (28 waves) per CU, the occupancy the kernel
+// reaches at 70 VGPRs without spilling.
+constexpr int kBcBlocksPerCu = 7;
+// Copies longer than this are published in a queue and split into kBcChunk
+// pieces dealt over all waves; shorter ones are copied whole by their owner.
 constexpr uint64_t kBcSplitAbove = 64 * 1024;
-constexpr uint64_t kBcChunk = 32 * 1024;
-// Capacity of the large-copy queue; copies beyond it run on their owner wave.
+constexpr uint64_t kBcChunk = 8 * 1024;
+// Capacity of the long-copy queue; copies beyond it are copied by the
+// scanning wave that found them.
 constexpr uint32_t kBcQueueCap = 16384;
-
-struct BcSlot {
-    uint32_t desc_plus1;   // 0 = not yet published
-    uint32_t next_chunk;   // next unclaimed chunk
-};
+// Descriptors scanned per scanner workgroup (the first workgroups of the grid).
+constexpr uint32_t kBcScanPerBlock = 1024;
+// Longest wait for the queue to be sealed, in microseconds of device time.
+constexpr uint32_t kBcSealWaitUs = 200;
 
 struct alignas(256) BcCounter {
     uint32_t count;
@@ -58,21 +61,24 @@ struct alignas(256) BcCounter {
 };
 
 struct BcScratch {
-    uint32_t qtail;        // slots handed out (may exceed kBcQueueCap)
-    uint32_t done_all;     // XCD groups finished
-    uint32_t pad[62];      // keep these counters on their own 256 bytes
-    BcCounter done_xcd[8]; // workgroups finished, per XCD (blockIdx % 8)
-    BcSlot slot[kBcQueueCap];
+    BcCounter qtail;        // queue slots handed out (may exceed kBcQueueCap)
+    BcCounter scan_done;    // scanner workgroups finished
+    BcCounter fallback;     // set when a wave gave up waiting: redo the queue
+    BcCounter done_all;     // XCD groups finished
+    BcCounter done_xcd[8];  // workgroups finished, per XCD (blockIdx % 8)
+    uint32_t slot[kBcQueueCap];  // descriptor index + 1 of each queued copy
 };
 
 constexpr size_t kBcScratchBytes = sizeof(BcScratch);
 
 int batched_grid(int cu_count);
+uint32_t batched_scanners(uint32_t ncopies, int grid);
 
 // Enqueue the batched copy.  `scratch` must be kBcScratchBytes of device
 // memory that was zeroed once; the kernel leaves it zeroed again.
+// wait_ticks: kBcSealWaitUs in ticks of the device wall clock.
 hipError_t launch_batched_copy(const tb_copy_desc *desc, uint32_t n, BcScratch *scratch,
-                               int cu_count, hipStream_t stream);
+                               int cu_count, uint64_t wait_ticks, hipStream_t stream);
 
 // ---- spin gate ---------------------------------------------------------------
 

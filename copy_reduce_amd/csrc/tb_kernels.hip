@@ -355,39 +355,49 @@ constexpr int kBcStorePol = kPolNt | kPolSc0 | kPolSc1;
 
 // Copy n elements of E bytes from s to d with the whole wave (s, d, n
 // wave-uniform; s and d E-byte aligned).  Each step covers kBcUnroll slots of
-// 64 elements and issues all its loads back to back before its stores.  Every
-// slot has its own raw buffer resource over exactly the bytes it may touch
-// (possibly none), addressed by the lane offset alone: the hardware range
-// check covers the voffset (not the scalar soffset), so lanes past the end of
-// the copy read zero and their stores are dropped, and no access ever leaves
-// [s, s + n E) or [d, d + n E).  No predication, one VGPR of addressing.
+// 64 elements and issues all its loads back to back before its stores, through
+// one raw buffer resource per direction: the lane offset is the only VGPR
+// operand and the slot offset goes in the scalar soffset.  Full steps touch
+// only bytes inside the copy; in the last, partial step each lane is
+// predicated on its element lying inside the copy, so no access ever leaves
+// [s, s + nE) or [d, d + nE) (the resource bounds are a second guard).
 template <int E>
 __device__ __forceinline__ void wave_copy_buf(uint64_t s, uint64_t d, uint64_t n, int lane) {
     typedef typename BufElem<E>::T T;
-    constexpr uint64_t kSlot = 64 * E;                 // bytes per slot
-    constexpr uint64_t kStepBytes = kSlot * kBcUnroll;
+    constexpr uint32_t kSlot = 64 * E;                 // bytes per slot
+    constexpr uint64_t kStepBytes = (uint64_t)kSlot * kBcUnroll;
     const uint64_t total = n * E;
-    for (uint64_t b0 = 0; b0 < total; b0 += kStepBytes) {
-        const uint64_t left = total - b0;
+    uint64_t b0 = 0;
+    for (; b0 + kStepBytes <= total; b0 += kStepBytes) {
+        const __amdgpu_buffer_rsrc_t in = buffer_over(s + b0, (uint32_t)kStepBytes);
+        const __amdgpu_buffer_rsrc_t out = buffer_over(d + b0, (uint32_t)kStepBytes);
         T r[kBcUnroll];
 #pragma unroll
-        for (int u = 0; u < kBcUnroll; u++) {
-            const uint64_t off = (uint64_t)u * kSlot;
-            const uint32_t rec = left > off ? (uint32_t)(left - off < kSlot ? left - off : kSlot) : 0u;
-            r[u] = BufElem<E>::template load<kBcLoadPol>(buffer_over(s + b0 + off, rec), lane * E, 0);
-        }
+        for (int u = 0; u < kBcUnroll; u++)
+            r[u] = BufElem<E>::template load<kBcLoadPol>(in, lane * E, u * kSlot);
 #pragma unroll
-        for (int u = 0; u < kBcUnroll; u++) {
-            const uint64_t off = (uint64_t)u * kSlot;
-            const uint32_t rec = left > off ? (uint32_t)(left - off < kSlot ? left - off : kSlot) : 0u;
-            BufElem<E>::template store<kBcStorePol>(r[u], buffer_over(d + b0 + off, rec), lane * E, 0);
-        }
+        for (int u = 0; u < kBcUnroll; u++)
+            BufElem<E>::template store<kBcStorePol>(r[u], out, lane * E, u * kSlot);
+    }
+    if (b0 < total) {
+        const uint32_t left = (uint32_t)(total - b0);
+        const __amdgpu_buffer_rsrc_t in = buffer_over(s + b0, left);
+        const __amdgpu_buffer_rsrc_t out = buffer_over(d + b0, left);
+        T r[kBcUnroll];
+#pragma unroll
+        for (int u = 0; u < kBcUnroll; u++)
+            if (u * kSlot + (uint32_t)lane * E < left)
+                r[u] = BufElem<E>::template load<kBcLoadPol>(in, lane * E, u * kSlot);
+#pragma unroll
+        for (int u = 0; u < kBcUnroll; u++)
+            if (u * kSlot + (uint32_t)lane * E < left)
+                BufElem<E>::template store<kBcStorePol>(r[u], out, lane * E, u * kSlot);
     }
 }
 
-// Up to 63 single bytes, one per lane (range-checked: lanes past n do nothing).
+// Up to 15 single bytes, one per lane (lanes at or past n do nothing).
 __device__ __forceinline__ void wave_copy_few_bytes(uint64_t s, uint64_t d, uint64_t n, int lane) {
-    if (n == 0)
+    if ((uint64_t)lane >= n)
         return;
     const __amdgpu_buffer_rsrc_t in = buffer_over(s, (uint32_t)n);
     const __amdgpu_buffer_rsrc_t out = buffer_over(d, (uint32_t)n);
@@ -397,8 +407,10 @@ __device__ __forceinline__ void wave_copy_few_bytes(uint64_t s, uint64_t d, uint
 // Copy b bytes from s to d with the whole wave; s, d, b are wave-uniform.
 // 16-byte elements when s and d agree modulo 16 (bytes before dst's first
 // 16-byte boundary and after the last one go one per lane), dwords when they
-// agree modulo 4, single bytes otherwise.
-__device__ __forceinline__ void wave_copy(uint64_t s, uint64_t d, uint64_t b, int lane) {
+// agree modulo 4, single bytes otherwise.  Not inlined: it serves the rare
+// cases, and keeping it out of the kernel body keeps the hot path's register
+// allocation small.
+__device__ __noinline__ void wave_copy_any(uint64_t s, uint64_t d, uint64_t b, int lane) {
     const uint64_t mis = (s ^ d) & 15;
     if (mis != 0 && (mis & 3) != 0) {
         wave_copy_buf<1>(s, d, b, lane);
@@ -420,6 +432,18 @@ __device__ __forceinline__ void wave_copy(uint64_t s, uint64_t d, uint64_t b, in
     wave_copy_few_bytes(s + body, d + body, b - body, lane);
 }
 
+// Hot path: both ends 16-byte aligned (every copy of the KV-transfer shapes);
+// anything else goes to wave_copy_any.
+__device__ __forceinline__ void wave_copy(uint64_t s, uint64_t d, uint64_t b, int lane) {
+    if (((s | d) & 15) == 0) {
+        const uint64_t body = b & ~(uint64_t)15;
+        wave_copy_buf<16>(s, d, body >> 4, lane);
+        wave_copy_few_bytes(s + body, d + body, b - body, lane);
+    } else {
+        wave_copy_any(s, d, b, lane);
+    }
+}
+
 __device__ __forceinline__ uint32_t atomic_load_agent(const uint32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -432,31 +456,70 @@ __device__ __forceinline__ uint32_t atomic_add_agent(uint32_t *p, uint32_t v) {
     return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_copy_desc *__restrict__ desc,
-                                                      uint32_t n, BcScratch *scr) {
-    const int lane = threadIdx.x & 63;
-    const uint64_t W = (uint64_t)gridDim.x * (kBcBlock / 64);
-    const uint64_t wave = (uint64_t)blockIdx.x * (kBcBlock / 64) + (threadIdx.x >> 6);
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o, 64);
+        if (lane >= o)
+            x += y;
+    }
+    return x;
+}
 
-    // ---- own descriptors: publish the long ones, copy the rest ----
+__global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_copy_desc *__restrict__ desc,
+                                                                      uint32_t n, BcScratch *scr,
+                                                                      uint32_t scanners, uint64_t wait_ticks) {
+    const int lane = threadIdx.x & 63;
+    // wave-uniform values kept in scalar registers (readfirstlane tells the
+    // compiler so; otherwise their arithmetic would run per lane)
+    const uint32_t wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t W = gridDim.x * (kBcBlock / 64);
+    const uint32_t wave = blockIdx.x * (kBcBlock / 64) + wave_in_block;
+
+    // ---- 1. The first `scanners` workgroups (dispatched first) find the long
+    // copies and publish them; a copy that no longer fits the queue is copied
+    // here, by the wave that found it. ----
+    if (blockIdx.x < scanners) {
+        const uint64_t per = ((uint64_t)n + scanners - 1) / scanners;
+        const uint64_t lo = (uint64_t)blockIdx.x * per;
+        const uint64_t hi = lo + per < n ? lo + per : n;
+        for (uint64_t b0 = lo + (uint64_t)wave_in_block * 64; b0 < hi; b0 += kBcBlock) {
+            const uint64_t i = b0 + lane;
+            bool here = false;
+            if (i < hi && desc[i].bytes > kBcSplitAbove) {
+                const uint32_t slot = atomic_add_agent(&scr->qtail.count, 1u);
+                if (slot < kBcQueueCap)
+                    atomic_store_agent(&scr->slot[slot], (uint32_t)i + 1u);
+                else
+                    here = true;
+            }
+            uint64_t todo = __ballot(here);
+            while (todo) {
+                const int j = __builtin_ctzll(todo);
+                todo &= todo - 1;
+                const uint64_t di = readlane_u64(i, j);
+                wave_copy_any(readfirstlane_u64(desc[di].src), readfirstlane_u64(desc[di].dst),
+                              readfirstlane_u64(desc[di].bytes), lane);
+            }
+        }
+        __syncthreads();   // every slot store of this workgroup has completed
+        if (threadIdx.x == 0)
+            atomic_add_agent(&scr->scan_done.count, 1u);
+    }
+
+    // ---- 2. Own descriptors w, w + W, ...: copy the short ones whole (the
+    // long ones belong to the queue).  Up to 64 fetched with one load per
+    // lane, then broadcast to the whole wave. ----
     for (uint64_t k0 = 0; wave + k0 * W < n; k0 += 64) {
-        const uint64_t i = wave + (k0 + lane) * W;
-        const bool valid = i < n;
+        const uint64_t i = wave + (k0 + lane) * (uint64_t)W;
         uint64_t s = 0, d = 0, b = 0;
-        if (valid) {
+        if (i < n) {
             s = desc[i].src;
             d = desc[i].dst;
             b = desc[i].bytes;
         }
-        bool run_here = valid && b != 0;
-        if (valid && b > kBcSplitAbove) {
-            const uint32_t slot = atomic_add_agent(&scr->qtail, 1u);
-            if (slot < kBcQueueCap) {
-                atomic_store_agent(&scr->slot[slot].desc_plus1, (uint32_t)i + 1u);
-                run_here = false;
-            }
-        }
-        uint64_t todo = __ballot(run_here);
+        uint64_t todo = __ballot(b != 0 && b <= kBcSplitAbove);
         while (todo) {
             const int j = __builtin_ctzll(todo);
             todo &= todo - 1;
@@ -464,44 +527,71 @@ __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_c
         }
     }
 
-    // ---- help with the published long copies ----
-    uint32_t seen = 0;
-    for (;;) {
-        uint32_t q = atomic_load_agent(&scr->qtail);
-        q = __builtin_amdgcn_readfirstlane(q < kBcQueueCap ? q : kBcQueueCap);
-        if (q <= seen)
-            break;
-        const uint32_t span = q - seen;
-        for (uint32_t r = 0; r < span; r++) {
-            const uint32_t e = seen + (uint32_t)((r + wave) % span);
-            const uint32_t v = __builtin_amdgcn_readfirstlane(atomic_load_agent(&scr->slot[e].desc_plus1));
-            if (v == 0)
-                continue;   // not published yet: its owner will copy it
-            const uint64_t di = v - 1u;
-            const uint64_t s = readfirstlane_u64(desc[di].src);
-            const uint64_t d = readfirstlane_u64(desc[di].dst);
-            const uint64_t b = readfirstlane_u64(desc[di].bytes);
-            const uint64_t nchunks = (b + kBcChunk - 1) / kBcChunk;
-            for (;;) {
-                uint32_t c = 0;
-                if (lane == 0)
-                    c = atomic_add_agent(&scr->slot[e].next_chunk, 1u);
-                c = __builtin_amdgcn_readfirstlane(c);
-                if (c >= nchunks)
-                    break;
-                const uint64_t off = (uint64_t)c * kBcChunk;
-                const uint64_t len = b - off < kBcChunk ? b - off : kBcChunk;
-                wave_copy(s + off, d + off, len, lane);
+    // ---- 3. Wait (bounded) until every scanner has finished: the queue is
+    // then complete and the same for every wave.  Its kBcChunk pieces are
+    // numbered across all entries and piece g goes to wave g mod W, so no
+    // atomics are needed to share them.  A wave that gives up waiting, or
+    // finds a slot not yet visible, sets the fallback flag instead. ----
+    bool sealed = false;
+    {
+        const uint64_t t0 = wall_clock64();
+        for (;;) {
+            if ((uint32_t)__builtin_amdgcn_readfirstlane(atomic_load_agent(&scr->scan_done.count)) >= scanners) {
+                sealed = true;
+                break;
             }
+            if (wall_clock64() - t0 > wait_ticks)
+                break;
+            __builtin_amdgcn_s_sleep(4);
         }
-        seen = q;
     }
+    if (sealed) {
+        uint32_t q = __builtin_amdgcn_readfirstlane(atomic_load_agent(&scr->qtail.count));
+        if (q > kBcQueueCap)
+            q = kBcQueueCap;
+        uint32_t base_mod = 0;   // (number of the first piece of this group) mod W
+        for (uint32_t g0 = 0; g0 < q && sealed; g0 += 64) {
+            // lane l holds entry g0 + l: its descriptor index and piece count
+            const uint32_t e = g0 + lane;
+            uint32_t v = 0, npieces = 0;
+            bool missing = false;
+            if (e < q) {
+                v = atomic_load_agent(&scr->slot[e]);
+                if (v == 0)
+                    missing = true;
+                else
+                    npieces = (uint32_t)((desc[v - 1].bytes + kBcChunk - 1) / kBcChunk);
+            }
+            if (__ballot(missing)) {
+                sealed = false;
+                break;
+            }
+            const uint32_t incl = wave_inclusive_sum(npieces, lane);
+            const uint32_t excl = incl - npieces;
+            const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
+            // this wave's pieces: g = base + r with g = wave (mod W)
+            for (uint32_t r = (wave + W - base_mod) % W; r < total; r += W) {
+                const uint64_t owners = __ballot(e < q && excl <= r);
+                const int j = 63 - __builtin_clzll(owners);
+                const uint64_t c = r - (uint32_t)__builtin_amdgcn_readlane(excl, j);   // piece within entry j
+                const uint64_t di = (uint32_t)__builtin_amdgcn_readlane(v, j) - 1u;
+                const uint64_t bj = readfirstlane_u64(desc[di].bytes);
+                const uint64_t off = c * kBcChunk;
+                wave_copy(readfirstlane_u64(desc[di].src) + off, readfirstlane_u64(desc[di].dst) + off,
+                          bj - off < kBcChunk ? bj - off : kBcChunk, lane);
+            }
+            base_mod = (uint32_t)(((uint64_t)base_mod + total) % W);
+        }
+    }
+    if (!sealed && lane == 0)
+        atomic_store_agent(&scr->fallback.count, 1u);
 
-    // ---- completion: the last workgroup out clears the queue for the next
-    // launch.  Workgroups count in per-XCD counters (gridDim.x is a multiple
-    // of 8, so each XCD group has gridDim.x / 8 members); the last of each
-    // group then counts in one counter for the 8 groups.  This keeps 2,048
-    // workgroups from serialising on one address. ----
+    // ---- 4. Completion.  Workgroups count in per-XCD counters (gridDim.x is
+    // a multiple of 8, so each XCD group has gridDim.x / 8 members), the last
+    // of each group in one counter for the 8 groups: 2,048 workgroups never
+    // serialise on one address.  The last workgroup out redoes the whole queue
+    // if any wave fell back (identical bytes written again), then clears the
+    // scratch for the next launch. ----
     __shared__ uint32_t last_block;
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -509,36 +599,55 @@ __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_c
         const uint32_t x = blockIdx.x & 7;
         if (atomic_add_agent(&scr->done_xcd[x].count, 1u) == gridDim.x / 8 - 1) {
             atomic_store_agent(&scr->done_xcd[x].count, 0u);
-            last = atomic_add_agent(&scr->done_all, 1u) == 7 ? 1u : 0u;
+            last = atomic_add_agent(&scr->done_all.count, 1u) == 7 ? 1u : 0u;
         }
         last_block = last;
     }
     __syncthreads();
     if (last_block) {
-        uint32_t q = atomic_load_agent(&scr->qtail);
+        uint32_t q = __builtin_amdgcn_readfirstlane(atomic_load_agent(&scr->qtail.count));
         if (q > kBcQueueCap)
             q = kBcQueueCap;
-        for (uint32_t e = threadIdx.x; e < q; e += kBcBlock) {
-            atomic_store_agent(&scr->slot[e].desc_plus1, 0u);
-            atomic_store_agent(&scr->slot[e].next_chunk, 0u);
+        if (__builtin_amdgcn_readfirstlane(atomic_load_agent(&scr->fallback.count)) != 0) {
+            for (uint32_t e = threadIdx.x >> 6; e < q; e += kBcBlock / 64) {
+                const uint32_t v = __builtin_amdgcn_readfirstlane(atomic_load_agent(&scr->slot[e]));
+                if (v != 0)
+                    wave_copy_any(readfirstlane_u64(desc[v - 1].src), readfirstlane_u64(desc[v - 1].dst),
+                                  readfirstlane_u64(desc[v - 1].bytes), lane);
+            }
         }
+        for (uint32_t e = threadIdx.x; e < q; e += kBcBlock)
+            atomic_store_agent(&scr->slot[e], 0u);
         __syncthreads();
         if (threadIdx.x == 0) {
-            atomic_store_agent(&scr->qtail, 0u);
-            atomic_store_agent(&scr->done_all, 0u);
+            atomic_store_agent(&scr->qtail.count, 0u);
+            atomic_store_agent(&scr->scan_done.count, 0u);
+            atomic_store_agent(&scr->fallback.count, 0u);
+            atomic_store_agent(&scr->done_all.count, 0u);
         }
     }
 }
 
 int batched_grid(int cu_count) {
-    // a multiple of 8 (the completion counters are per XCD)
-    return (cu_count > 0 ? cu_count : 1) * kBcBlocksPerCu;
+    // rounded up to a multiple of 8 (the completion counters are per XCD)
+    const int g = (cu_count > 0 ? cu_count : 1) * kBcBlocksPerCu;
+    return (g + 7) & ~7;
 }
 
-hipError_t launch_batched_copy(const tb_copy_desc *desc, uint32_t n, BcScratch *scratch,
-                               int cu_count, hipStream_t s) {
-    hipLaunchKernelGGL(bc_kernel, dim3(batched_grid(cu_count)), dim3(kBcBlock), 0, s, desc, n,
-                       scratch);
+uint32_t batched_scanners(uint32_t ncopies, int grid) {
+    uint32_t s = (ncopies + kBcScanPerBlock - 1) / kBcScanPerBlock;
+    if (s < 1)
+        s = 1;
+    if (s > (uint32_t)grid)
+        s = (uint32_t)grid;
+    return s;
+}
+
+hipError_t launch_batched_copy(const tb_copy_desc *desc, uint32_t n, BcScratch *scratch, int cu_count,
+                               uint64_t wait_ticks, hipStream_t s) {
+    const int grid = batched_grid(cu_count);
+    hipLaunchKernelGGL(bc_kernel, dim3(grid), dim3(kBcBlock), 0, s, desc, n, scratch,
+                       batched_scanners(n, grid), wait_ticks);
     return hipGetLastError();
 }
 
