@@ -154,7 +154,7 @@ def main_line(args, torch, tb, wl):
     rc_mean, bc_mean = statistics.mean(rc_ms), statistics.mean(bc_ms)
     rc_gbps = rc_bytes / (rc_mean * 1e-3) / 1e9
     bc_gbps = bc_bytes / (bc_mean * 1e-3) / 1e9
-    info = tb.tb_launch_info(w.nfloats, w.nsrc)
+    info = tb.tb_launch_info(w.nfloats, w.nsrc, batch.ncopies)
     traffic = _traffic("reduce_copy")
 
     line = {
@@ -264,26 +264,38 @@ def suite(args, torch, tb, wl):
     sh = stream.cuda_stream
     timer = Timed(torch, tb, stream)
 
-    def reduce_line(w, reps=1):
+    def reduce_line(w, reps=1, rotate_dst=False):
+        """rotate_dst: also rotate the destination over K slices (same rule as the
+        sources).  Not the pages' method (they rotate sources only); it shows
+        the rate with a destination that is not resident in the memory-side cache."""
         rs, dst = setup_reduce(torch, w)
-        dptr = int(dst.data_ptr())
+        kd = rs.k if rotate_dst else 1
+        dsts = torch.empty(max(1, kd * rs.stride), dtype=torch.uint8, device="cuda") if rotate_dst else None
+        dbase = int(dsts.data_ptr()) if rotate_dst else int(dst.data_ptr())
+
+        def dptr_for(i):
+            if not rotate_dst:
+                return dbase
+            return tb.tb_rotate_sources([dbase], rs.stride, kd, i)[0]
+
         means = []
         for _ in range(reps):
             for i in range(-args.warmup, 0):
-                tb.tb_reduce_copy(dptr, rs.pointers(i), w.nfloats, sh)
+                tb.tb_reduce_copy(dptr_for(i), rs.pointers(i), w.nfloats, sh)
             launches = []
             for i in range(args.steps):
-                ptrs = rs.pointers(i)
-                launches.append(lambda p=ptrs: tb.tb_reduce_copy(dptr, p, w.nfloats, sh))
+                ptrs, dp = rs.pointers(i), dptr_for(i)
+                launches.append(lambda p=ptrs, dp=dp: tb.tb_reduce_copy(dp, p, w.nfloats, sh))
             ms, total, _ = timer.run(launches)
             means.append((statistics.mean(ms), min(ms), max(ms), total))
         med = sorted(means)[len(means) // 2]
         gbps = w.algorithmic_bytes / (med[0] * 1e-3) / 1e9
-        out = {"config": w.name, "nsrc": w.nsrc, "nfloats": w.nfloats, "k": rs.k, "reps": reps,
+        out = {"config": w.name + ("_dstrot" if rotate_dst else ""), "nsrc": w.nsrc, "nfloats": w.nfloats,
+               "k": rs.k, "reps": reps,
                "ms_mean": round(med[0], 5), "ms_min": round(med[1], 5), "ms_max": round(med[2], 5),
                "gbps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
                "aggregate_gbps": round(args.steps * w.algorithmic_bytes / (med[3] * 1e-3) / 1e9, 1)}
-        del rs, dst
+        del rs, dst, dsts
         torch.cuda.empty_cache()
         return out
 
@@ -307,9 +319,14 @@ def suite(args, torch, tb, wl):
         torch.cuda.empty_cache()
         return out
 
-    for name in ("c1_copy_4MiB_rot", "c2_reduce2_256MiB_rot", "c2_reduce2_256MiB_norot",
+    for name in ("c1_copy_4MiB_rot", "c1_copy_4MiB_norot", "c2_reduce2_256MiB_rot", "c2_reduce2_256MiB_norot",
                  "c3_reduce4_64MiB_compress"):
         print(json.dumps({"suite": reduce_line(wl.REDUCE_CONFIGS[name])}), flush=True)
+    # controls beyond the pages' method: destination rotated too (R = 1 GiB for C2 so that K > 1)
+    c2cold = wl.ReduceWorkload("c2_reduce2_256MiB_R1GiB", 2, 64 << 20, 4 * wl.DEFAULT_ROTATE_BYTES)
+    print(json.dumps({"suite": reduce_line(c2cold)}), flush=True)
+    print(json.dumps({"suite": reduce_line(c2cold, rotate_dst=True)}), flush=True)
+    print(json.dumps({"suite": reduce_line(wl.REDUCE_CONFIGS["c3_reduce4_64MiB_compress"], rotate_dst=True)}), flush=True)
     c4 = wl.batch_c4()
     print(json.dumps({"suite": batch_line(c4, wl.DEFAULT_ROTATE_BYTES, "rotated")}), flush=True)
     print(json.dumps({"suite": batch_line(c4, 0, "control")}), flush=True)

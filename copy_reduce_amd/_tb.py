@@ -66,7 +66,7 @@ _SIGS = {
     "tb_spin_gate_arm": (ctypes.c_int, [_u32, _vp]),
     "tb_spin_gate_release": (ctypes.c_int, []),
     "tb_spin_gate_status": (ctypes.c_int, []),
-    "tb_launch_info": (ctypes.c_int, [_u64, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32),
+    "tb_launch_info": (ctypes.c_int, [_u64, _i32, _u32, ctypes.POINTER(_i32), ctypes.POINTER(_i32),
                                       ctypes.POINTER(_i32)]),
     "tb_shutdown": (ctypes.c_int, []),
 }
@@ -151,9 +151,10 @@ def tb_status_string(status: int) -> str:
     return lib.tb_status_string(status).decode()
 
 
-def tb_launch_info(nfloats: int = 0, nsrc: int = 1):
+def tb_launch_info(nfloats: int = 0, nsrc: int = 1, ncopies: int = 0):
     cu, rb, bb = _i32(), _i32(), _i32()
-    _check("tb_launch_info", lib.tb_launch_info(nfloats, nsrc, ctypes.byref(cu), ctypes.byref(rb), ctypes.byref(bb)))
+    _check("tb_launch_info", lib.tb_launch_info(nfloats, nsrc, ncopies, ctypes.byref(cu), ctypes.byref(rb),
+                                                ctypes.byref(bb)))
     return {"cu_count": cu.value, "reduce_blocks": rb.value, "batched_blocks": bb.value}
 
 

@@ -309,8 +309,8 @@ int tb_spin_gate_status(void) {
     return __atomic_load_n(&g_gate[1], __ATOMIC_SEQ_CST) ? TB_ERR_TIMEOUT : TB_OK;
 }
 
-int tb_launch_info(uint64_t nfloats, int32_t nsrc, int32_t *cu_count, int32_t *reduce_blocks,
-                   int32_t *batched_blocks) {
+int tb_launch_info(uint64_t nfloats, int32_t nsrc, uint32_t ncopies, int32_t *cu_count,
+                   int32_t *reduce_blocks, int32_t *batched_blocks) {
     if (nsrc < 0 || nsrc > TB_MAX_SRCS)
         return TB_ERR_INVALID;
     DeviceInfo info;
@@ -322,7 +322,7 @@ int tb_launch_info(uint64_t nfloats, int32_t nsrc, int32_t *cu_count, int32_t *r
     if (reduce_blocks)
         *reduce_blocks = tbk::reduce_grid(nfloats, nsrc, true, info.cu_count);
     if (batched_blocks)
-        *batched_blocks = tbk::batched_grid(info.cu_count);
+        *batched_blocks = tbk::batched_grid(ncopies, info.cu_count);
     return TB_OK;
 }
 

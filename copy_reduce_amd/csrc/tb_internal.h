@@ -40,9 +40,18 @@ hipError_t launch_reduce_copy(const ReduceArgs &args, int nsrc, bool vector_path
 // ---- batched copy ------------------------------------------------------------
 
 constexpr int kBcBlock = 256;        // 4 wave64s per workgroup
-// Persistent grid: 7 workgroups (28 waves) per CU, the occupancy the kernel
-// reaches at 70 VGPRs without spilling.
+// Occupancy: 7 workgroups (28 waves) per CU is what the kernel reaches at
+// 72 VGPRs without spilling; the waves resident from the start share the
+// pieces of long copies.
 constexpr int kBcBlocksPerCu = 7;
+constexpr uint32_t kBcResidentWavesPerCu = kBcBlocksPerCu * (kBcBlock / 64);
+// Launched grid: about kBcDescPerWave descriptors per wave, between the
+// resident count (kBcBlocksPerCu per CU) and kBcMaxGridPerCu per CU.  More
+// workgroups than resident let the dispatcher hand finished CUs new work
+// (+3-5% on the 47,520-copy batch); on small batches extra workgroups only
+// add scan and completion overhead (-9% on the 11,044-copy batch at 16/CU).
+constexpr int kBcMaxGridPerCu = 16;
+constexpr uint32_t kBcDescPerWave = 3;
 // Copies longer than this are published in a queue and split into kBcChunk
 // pieces dealt over all waves; shorter ones are copied whole by their owner.
 constexpr uint64_t kBcSplitAbove = 64 * 1024;
@@ -71,7 +80,7 @@ struct BcScratch {
 
 constexpr size_t kBcScratchBytes = sizeof(BcScratch);
 
-int batched_grid(int cu_count);
+int batched_grid(uint32_t ncopies, int cu_count);
 uint32_t batched_scanners(uint32_t ncopies, int grid);
 
 // Enqueue the batched copy.  `scratch` must be kBcScratchBytes of device

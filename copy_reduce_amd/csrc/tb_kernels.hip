@@ -51,6 +51,11 @@ constexpr int rc_unroll() {
     return N <= 2 ? 1 : (N <= 4 ? 2 : 1);
 }
 
+template <int N>
+constexpr bool rc_xcd_map() {
+    return N <= 2;
+}
+
 // Sources are streamed once per launch: nontemporal loads (without them the
 // kernel measured 73% of peak instead of 92%).  Results are written with
 // device-scope (sc1) stores, through L2 to the memory side: measured faster
@@ -58,11 +63,13 @@ constexpr int rc_unroll() {
 __device__ __forceinline__ f32x4 rc_load(const gf32x4 *p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ float rc_load(const gf32 *p) { return __builtin_nontemporal_load(p); }
 
-// Workgroup b runs on XCD b % 8 (round-robin dispatch).  Give each XCD one
-// contiguous eighth of the tiles, walked in order, instead of every eighth
-// tile: measured faster on the streaming kernels.  `v` is the virtual block
-// index in [0, 8 * ceil(ntiles / 8)); returns false for the few virtual blocks
-// that have no tile.  A bijection onto [0, ntiles).
+// Workgroup b runs on XCD b % 8 (round-robin dispatch).  xcd_tile gives each
+// XCD one contiguous eighth of the tiles, walked in order, instead of every
+// eighth tile.  `v` is the virtual block index in [0, 8 * ceil(ntiles / 8));
+// returns false for the few virtual blocks that have no tile.  A bijection
+// onto [0, ntiles).  Measured on MI355X (cold destination): +3 points for two
+// sources, equal for one, and 2-7 points slower from three sources up (eight
+// regions times N + 1 streams at once), so it is used only for N <= 2.
 __device__ __forceinline__ bool xcd_tile(uint64_t v, uint64_t ntiles, uint64_t *tile) {
     const uint64_t q = ntiles >> 3, r = ntiles & 7;
     const uint64_t x = v & 7, k = v >> 3;
@@ -101,10 +108,10 @@ __global__ __launch_bounds__(kRcBlock) void rc_vec_kernel(ReduceArgs a) {
     for (int k = 0; k < N; k++)
         src[k] = (const gf32x4 *)(a.src[k] + a.head);
 
-    const uint64_t vend = virtual_blocks(ntiles);
+    const uint64_t vend = rc_xcd_map<N>() ? virtual_blocks(ntiles) : ntiles;
     for (uint64_t v = blockIdx.x; v < vend; v += gridDim.x) {
-        uint64_t t;
-        if (!xcd_tile(v, ntiles, &t))
+        uint64_t t = v;
+        if (rc_xcd_map<N>() && !xcd_tile(v, ntiles, &t))
             continue;
         const uint64_t base = t * kTile;
         const uint64_t i0 = base + threadIdx.x;
@@ -469,7 +476,8 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x, int lane) {
 
 __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_copy_desc *__restrict__ desc,
                                                                       uint32_t n, BcScratch *scr,
-                                                                      uint32_t scanners, uint64_t wait_ticks) {
+                                                                      uint32_t scanners, uint64_t wait_ticks,
+                                                                      uint32_t piece_waves) {
     const int lane = threadIdx.x & 63;
     // wave-uniform values kept in scalar registers (readfirstlane tells the
     // compiler so; otherwise their arithmetic would run per lane)
@@ -545,6 +553,7 @@ __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_c
             __builtin_amdgcn_s_sleep(4);
         }
     }
+    const uint32_t P = piece_waves < W ? piece_waves : W;
     if (sealed) {
         uint32_t q = __builtin_amdgcn_readfirstlane(atomic_load_agent(&scr->qtail.count));
         if (q > kBcQueueCap)
@@ -569,8 +578,11 @@ __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_c
             const uint32_t incl = wave_inclusive_sum(npieces, lane);
             const uint32_t excl = incl - npieces;
             const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
-            // this wave's pieces: g = base + r with g = wave (mod W)
-            for (uint32_t r = (wave + W - base_mod) % W; r < total; r += W) {
+            // this wave's pieces: g = base + r with g = wave (mod P), for the
+            // first P waves (the ones resident from the start)
+            if (wave >= P)
+                break;
+            for (uint32_t r = (wave + P - base_mod) % P; r < total; r += P) {
                 const uint64_t owners = __ballot(e < q && excl <= r);
                 const int j = 63 - __builtin_clzll(owners);
                 const uint64_t c = r - (uint32_t)__builtin_amdgcn_readlane(excl, j);   // piece within entry j
@@ -580,7 +592,7 @@ __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_c
                 wave_copy(readfirstlane_u64(desc[di].src) + off, readfirstlane_u64(desc[di].dst) + off,
                           bj - off < kBcChunk ? bj - off : kBcChunk, lane);
             }
-            base_mod = (uint32_t)(((uint64_t)base_mod + total) % W);
+            base_mod = (uint32_t)(((uint64_t)base_mod + total) % P);
         }
     }
     if (!sealed && lane == 0)
@@ -628,10 +640,15 @@ __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_c
     }
 }
 
-int batched_grid(int cu_count) {
-    // rounded up to a multiple of 8 (the completion counters are per XCD)
-    const int g = (cu_count > 0 ? cu_count : 1) * kBcBlocksPerCu;
-    return (g + 7) & ~7;
+int batched_grid(uint32_t ncopies, int cu_count) {
+    const uint64_t cus = (uint64_t)(cu_count > 0 ? cu_count : 1);
+    uint64_t g = ((uint64_t)ncopies + kBcDescPerWave * 4 - 1) / (kBcDescPerWave * 4);
+    if (g < cus * kBcBlocksPerCu)
+        g = cus * kBcBlocksPerCu;
+    if (g > cus * kBcMaxGridPerCu)
+        g = cus * kBcMaxGridPerCu;
+    // a multiple of 8 (the completion counters are per XCD)
+    return (int)((g + 7) & ~(uint64_t)7);
 }
 
 uint32_t batched_scanners(uint32_t ncopies, int grid) {
@@ -645,9 +662,12 @@ uint32_t batched_scanners(uint32_t ncopies, int grid) {
 
 hipError_t launch_batched_copy(const tb_copy_desc *desc, uint32_t n, BcScratch *scratch, int cu_count,
                                uint64_t wait_ticks, hipStream_t s) {
-    const int grid = batched_grid(cu_count);
+    const int grid = batched_grid(n, cu_count);
+    // pieces of long copies go to the waves resident from the start: CUs x 8
+    // waves per SIMD x 4 SIMDs at most
+    const uint32_t resident = (uint32_t)(cu_count > 0 ? cu_count : 1) * kBcResidentWavesPerCu;
     hipLaunchKernelGGL(bc_kernel, dim3(grid), dim3(kBcBlock), 0, s, desc, n, scratch,
-                       batched_scanners(n, grid), wait_ticks);
+                       batched_scanners(n, grid), wait_ticks, resident);
     return hipGetLastError();
 }
 

@@ -204,12 +204,14 @@ int tb_spin_gate_release(void);
 int tb_spin_gate_status(void);
 
 /*
- * Launch geometry the library uses on the current device: compute units and
- * the workgroup counts of the reduce-copy and batched-copy kernels for the
- * given sizes (for reports; no GPU work is enqueued).  Any out pointer may be
- * NULL.  Errors: TB_ERR_HIP if the device cannot be queried.
+ * Launch geometry the library uses on the current device: compute units, the
+ * workgroup count of the reduce-copy for nfloats floats and nsrc sources, and
+ * that of the batched copy for ncopies descriptors (for reports; no GPU work
+ * is enqueued).  Any out pointer may be NULL.
+ * Errors: TB_ERR_INVALID for nsrc outside [0, TB_MAX_SRCS]; TB_ERR_HIP if the
+ * device cannot be queried.
  */
-int tb_launch_info(uint64_t nfloats, int32_t nsrc, int32_t *cu_count,
+int tb_launch_info(uint64_t nfloats, int32_t nsrc, uint32_t ncopies, int32_t *cu_count,
                    int32_t *reduce_blocks, int32_t *batched_blocks);
 
 /* Free the library's scratch and gate memory (waits for the device first).

@@ -56,6 +56,7 @@ C3_SEED = 3
 REDUCE_CONFIGS = {
     # single-source copy, 4 MiB, rotation on (K = 64)
     "c1_copy_4MiB_rot": ReduceWorkload("c1_copy_4MiB_rot", 1, 1 << 20, DEFAULT_ROTATE_BYTES),
+    "c1_copy_4MiB_norot": ReduceWorkload("c1_copy_4MiB_norot", 1, 1 << 20, 0),
     # two-source reduce, 256 MiB per buffer, rotation on (K = 1) and the R = 0 control
     "c2_reduce2_256MiB_rot": ReduceWorkload("c2_reduce2_256MiB_rot", 2, 64 << 20, DEFAULT_ROTATE_BYTES),
     "c2_reduce2_256MiB_norot": ReduceWorkload("c2_reduce2_256MiB_norot", 2, 64 << 20, 0),
