@@ -17,12 +17,13 @@ TB_ERR_NOMEM = -3
 TB_ERR_TIMEOUT = -4
 TB_MAX_SRCS = 16
 TB_FILL_DEFAULT, TB_FILL_PATTERN, TB_FILL_COMPRESS = 0, 1, 2
+TB_BC_NORMAL, TB_BC_NO_WAIT, TB_BC_LAST_ONLY = 0, 1, 2
 
 # Every symbol include/tb.h declares.
 EXPORTS = (
     "tb_num_slices", "tb_slice_stride", "tb_prep_reference", "tb_rotate_sources",
     "tb_status_string", "tb_last_hip_error", "tb_prep_sources", "tb_reduce_copy",
-    "tb_reduce_copy_ex", "tb_batched_copy", "tb_spin_gate_arm", "tb_spin_gate_release",
+    "tb_reduce_copy_ex", "tb_batched_copy", "tb_batched_set_mode", "tb_spin_gate_arm", "tb_spin_gate_release",
     "tb_spin_gate_status", "tb_launch_info", "tb_shutdown",
 )
 
@@ -63,6 +64,7 @@ _SIGS = {
     "tb_reduce_copy": (ctypes.c_int, [_vp, _vp, _i32, _u64, _vp]),
     "tb_reduce_copy_ex": (ctypes.c_int, [_vp, _vp, _i32, _u64, _u32, _vp]),
     "tb_batched_copy": (ctypes.c_int, [_vp, _u32, _vp]),
+    "tb_batched_set_mode": (ctypes.c_int, [_i32]),
     "tb_spin_gate_arm": (ctypes.c_int, [_u32, _vp]),
     "tb_spin_gate_release": (ctypes.c_int, []),
     "tb_spin_gate_status": (ctypes.c_int, []),
@@ -176,6 +178,10 @@ def tb_reduce_copy(dst_ptr: int, src_ptrs, nfloats: int, stream: int, memset_byt
 
 def tb_batched_copy(desc_dev_ptr: int, ncopies: int, stream: int) -> None:
     _check("tb_batched_copy", lib.tb_batched_copy(desc_dev_ptr, ncopies, stream))
+
+
+def tb_batched_set_mode(mode: int) -> None:
+    _check("tb_batched_set_mode", lib.tb_batched_set_mode(mode))
 
 
 def tb_spin_gate_arm(timeout_ms: int, stream: int) -> None:

@@ -1,5 +1,6 @@
 // tb_host.cpp -- host half of libtb: argument checks, slice geometry and
 // rotation, source preparation, launch dispatch, scratch and gate ownership.
+#include <atomic>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -247,6 +248,16 @@ int tb_reduce_copy(float *dst, const float *const *srcs, int32_t nsrc, uint64_t 
     return tb_reduce_copy_ex(dst, srcs, nsrc, nfloats, 0u, stream);
 }
 
+// How the batched copy shares its long copies (TB_BC_*): process-wide.
+static std::atomic<int> g_batched_mode{TB_BC_NORMAL};
+
+int tb_batched_set_mode(int32_t mode) {
+    if (mode != TB_BC_NORMAL && mode != TB_BC_NO_WAIT && mode != TB_BC_LAST_ONLY)
+        return TB_ERR_INVALID;
+    g_batched_mode.store(mode, std::memory_order_relaxed);
+    return TB_OK;
+}
+
 int tb_batched_copy(const tb_copy_desc *desc_dev, uint32_t ncopies, void *stream) {
     if (ncopies == 0)
         return TB_OK;
@@ -261,8 +272,11 @@ int tb_batched_copy(const tb_copy_desc *desc_dev, uint32_t ncopies, void *stream
     rc = scratch_for(s, &scratch);
     if (rc != TB_OK)
         return rc;
-    const uint64_t wait_ticks = (uint64_t)tbk::kBcSealWaitUs * info.wall_clock_khz / 1000u;
-    hipError_t e = tbk::launch_batched_copy(desc_dev, ncopies, scratch, info.cu_count, wait_ticks, s);
+    const int mode = g_batched_mode.load(std::memory_order_relaxed);
+    const uint64_t wait_ticks =
+        mode == TB_BC_NORMAL ? (uint64_t)tbk::kBcSealWaitUs * info.wall_clock_khz / 1000u : 0u;
+    hipError_t e = tbk::launch_batched_copy(desc_dev, ncopies, scratch, info.cu_count, wait_ticks,
+                                            mode == TB_BC_LAST_ONLY, s);
     if (e != hipSuccess)
         return hip_fail(e, "batched-copy launch");
     return TB_OK;

@@ -69,12 +69,18 @@ struct alignas(256) BcCounter {
     uint32_t pad[63];
 };
 
+struct alignas(256) BcWord {
+    uint64_t word;
+    uint64_t pad[31];
+};
+
 struct BcScratch {
-    BcCounter qtail;        // queue slots handed out (may exceed kBcQueueCap)
-    BcCounter scan_done;    // scanner workgroups finished
-    BcCounter fallback;     // set when a wave gave up waiting: redo the queue
-    BcCounter done_all;     // XCD groups finished
-    BcCounter done_xcd[8];  // workgroups finished, per XCD (blockIdx % 8)
+    BcWord scan;            // low 32 bits: queue slots handed out (may exceed
+                            // kBcQueueCap); high 32 bits: scanners finished
+    BcCounter done_all;     // bits 0-15: XCD groups finished; above: groups
+                            // with a wave that left the queue to the last one
+    BcCounter done_xcd[8];  // the same per XCD group (blockIdx % 8), counting
+                            // workgroups; at most 65,535 per group
     uint32_t slot[kBcQueueCap];  // descriptor index + 1 of each queued copy
 };
 
@@ -85,9 +91,11 @@ uint32_t batched_scanners(uint32_t ncopies, int grid);
 
 // Enqueue the batched copy.  `scratch` must be kBcScratchBytes of device
 // memory that was zeroed once; the kernel leaves it zeroed again.
-// wait_ticks: kBcSealWaitUs in ticks of the device wall clock.
+// wait_ticks: the longest wait for the queue, in ticks of the device wall
+// clock (normally kBcSealWaitUs).  no_pieces: no wave takes queue pieces, so
+// the last workgroup copies every queued copy (the recovery path, for tests).
 hipError_t launch_batched_copy(const tb_copy_desc *desc, uint32_t n, BcScratch *scratch,
-                               int cu_count, uint64_t wait_ticks, hipStream_t stream);
+                               int cu_count, uint64_t wait_ticks, bool no_pieces, hipStream_t stream);
 
 // ---- spin gate ---------------------------------------------------------------
 

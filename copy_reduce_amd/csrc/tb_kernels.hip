@@ -285,16 +285,18 @@ hipError_t launch_reduce_copy(const ReduceArgs &a, int nsrc, bool vector_path, i
 // (Mooncake RFC #5041, Design of #5040: one launch over a (src, dst, len)
 //  descriptor array; 16-byte vectors where the ranges allow.)
 //
-// Persistent grid of kBcBlocksPerCu workgroups per CU; the unit of work is a
-// wave64.  Wave w owns descriptors w, w + W, w + 2W, ... (W waves in all) and
-// fetches up to 64 of them with one load per lane.  It broadcasts each to the
-// whole wave (readlane, so addresses and lengths are scalar) and copies it
-// with 16-byte lanes, U loads in flight per lane before the matching stores.
-// Copies longer than kBcSplitAbove are published in a queue instead; after
-// its own small copies every wave claims kBcChunk pieces of queued copies
-// with one atomic per piece.  No wave ever waits for another: a queued copy
-// is always finished by the wave that published it, helpers only speed it
-// up.  The last workgroup to finish clears the queue for the next launch.
+// Persistent grid of 7 to 16 workgroups per CU (about 3 descriptors per
+// wave); the unit of work is a wave64.  Wave w owns descriptors w, w + W,
+// w + 2W, ... (W waves in all) and fetches up to 64 of them with one load per
+// lane.  It broadcasts each to the whole wave (readlane, so addresses and
+// lengths are scalar) and copies it with 16-byte lanes, 8 loads in flight per
+// lane before the matching stores.  Copies longer than kBcSplitAbove instead
+// go through a queue: the first workgroups scan the descriptors and publish
+// them, and once every scanner has finished the queue is cut into kBcChunk
+// pieces dealt round-robin to the resident waves, without atomics.  Every
+// wait is bounded: a wave that cannot see the finished queue in time leaves
+// its pieces, and the last workgroup to finish then copies the whole queue.
+// That workgroup also clears the scratch for the next launch.
 // ============================================================================
 
 constexpr int kBcUnroll = 8;   // 8 x 16 B x 64 lanes = 8 KiB per wave step
@@ -463,6 +465,18 @@ __device__ __forceinline__ uint32_t atomic_add_agent(uint32_t *p, uint32_t v) {
     return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+__device__ __forceinline__ uint64_t atomic_load_agent(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void atomic_store_agent(uint64_t *p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t atomic_add_agent(uint64_t *p, uint64_t v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x, int lane) {
 #pragma unroll
@@ -474,10 +488,16 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x, int lane) {
     return x;
 }
 
+// A queue slot holds descriptor index + 1; 0 (not yet visible) or anything
+// past the batch counts as missing.
+__device__ __forceinline__ bool slot_valid(uint32_t v, uint32_t n) {
+    return v != 0 && v <= n;
+}
+
 __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_copy_desc *__restrict__ desc,
                                                                       uint32_t n, BcScratch *scr,
                                                                       uint32_t scanners, uint64_t wait_ticks,
-                                                                      uint32_t piece_waves) {
+                                                                      uint32_t piece_waves, uint32_t no_pieces) {
     const int lane = threadIdx.x & 63;
     // wave-uniform values kept in scalar registers (readfirstlane tells the
     // compiler so; otherwise their arithmetic would run per lane)
@@ -486,8 +506,10 @@ __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_c
     const uint32_t wave = blockIdx.x * (kBcBlock / 64) + wave_in_block;
 
     // ---- 1. The first `scanners` workgroups (dispatched first) find the long
-    // copies and publish them; a copy that no longer fits the queue is copied
-    // here, by the wave that found it. ----
+    // copies and publish them.  Slots are claimed on the low half of the scan
+    // word; a copy that no longer fits the queue is copied here, by the wave
+    // that found it.  A finished scanner adds 1 to the high half once its
+    // slot stores have completed. ----
     if (blockIdx.x < scanners) {
         const uint64_t per = ((uint64_t)n + scanners - 1) / scanners;
         const uint64_t lo = (uint64_t)blockIdx.x * per;
@@ -496,7 +518,8 @@ __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_c
             const uint64_t i = b0 + lane;
             bool here = false;
             if (i < hi && desc[i].bytes > kBcSplitAbove) {
-                const uint32_t slot = atomic_add_agent(&scr->qtail.count, 1u);
+                // n < 2^32 claims in all, so the low half never carries
+                const uint32_t slot = (uint32_t)atomic_add_agent(&scr->scan.word, 1ull);
                 if (slot < kBcQueueCap)
                     atomic_store_agent(&scr->slot[slot], (uint32_t)i + 1u);
                 else
@@ -511,9 +534,14 @@ __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_c
                               readfirstlane_u64(desc[di].bytes), lane);
             }
         }
-        __syncthreads();   // every slot store of this workgroup has completed
+        // Each wave waits until its slot stores have completed (they are
+        // device-coherent atomic stores) before the barrier, so before thread
+        // 0 counts this workgroup as finished.  A release fence would do the
+        // same but also write back the whole L2 of the XCD.
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
         if (threadIdx.x == 0)
-            atomic_add_agent(&scr->scan_done.count, 1u);
+            atomic_add_agent(&scr->scan.word, 1ull << 32);
     }
 
     // ---- 2. Own descriptors w, w + W, ...: copy the short ones whole (the
@@ -535,17 +563,22 @@ __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_c
         }
     }
 
-    // ---- 3. Wait (bounded) until every scanner has finished: the queue is
-    // then complete and the same for every wave.  Its kBcChunk pieces are
-    // numbered across all entries and piece g goes to wave g mod W, so no
-    // atomics are needed to share them.  A wave that gives up waiting, or
-    // finds a slot not yet visible, sets the fallback flag instead. ----
+    // ---- 3. Wait (bounded) until every scanner has finished.  The queue
+    // length is then final, and it comes in the same word as the count of
+    // finished scanners, so every wave sees the same length.  The kBcChunk
+    // pieces are numbered across all entries and piece g goes to wave
+    // g mod P (P = the waves resident from the start), so no atomics are
+    // needed to share them.  A wave that gives up waiting, or meets a slot it
+    // cannot see yet, leaves the queue to the last workgroup instead. ----
     bool sealed = false;
-    {
+    uint32_t q = 0;
+    if (!no_pieces) {
         const uint64_t t0 = wall_clock64();
         for (;;) {
-            if ((uint32_t)__builtin_amdgcn_readfirstlane(atomic_load_agent(&scr->scan_done.count)) >= scanners) {
+            const uint64_t sw = readfirstlane_u64(atomic_load_agent(&scr->scan.word));
+            if ((uint32_t)(sw >> 32) >= scanners) {
                 sealed = true;
+                q = (uint32_t)sw < kBcQueueCap ? (uint32_t)sw : kBcQueueCap;
                 break;
             }
             if (wall_clock64() - t0 > wait_ticks)
@@ -555,10 +588,7 @@ __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_c
     }
     const uint32_t P = piece_waves < W ? piece_waves : W;
     if (sealed) {
-        uint32_t q = __builtin_amdgcn_readfirstlane(atomic_load_agent(&scr->qtail.count));
-        if (q > kBcQueueCap)
-            q = kBcQueueCap;
-        uint32_t base_mod = 0;   // (number of the first piece of this group) mod W
+        uint32_t base_mod = 0;   // (number of the first piece of this group) mod P
         for (uint32_t g0 = 0; g0 < q && sealed; g0 += 64) {
             // lane l holds entry g0 + l: its descriptor index and piece count
             const uint32_t e = g0 + lane;
@@ -566,7 +596,7 @@ __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_c
             bool missing = false;
             if (e < q) {
                 v = atomic_load_agent(&scr->slot[e]);
-                if (v == 0)
+                if (!slot_valid(v, n))
                     missing = true;
                 else
                     npieces = (uint32_t)((desc[v - 1].bytes + kBcChunk - 1) / kBcChunk);
@@ -579,7 +609,7 @@ __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_c
             const uint32_t excl = incl - npieces;
             const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
             // this wave's pieces: g = base + r with g = wave (mod P), for the
-            // first P waves (the ones resident from the start)
+            // first P waves
             if (wave >= P)
                 break;
             for (uint32_t r = (wave + P - base_mod) % P; r < total; r += P) {
@@ -595,46 +625,75 @@ __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_c
             base_mod = (uint32_t)(((uint64_t)base_mod + total) % P);
         }
     }
-    if (!sealed && lane == 0)
-        atomic_store_agent(&scr->fallback.count, 1u);
 
     // ---- 4. Completion.  Workgroups count in per-XCD counters (gridDim.x is
     // a multiple of 8, so each XCD group has gridDim.x / 8 members), the last
-    // of each group in one counter for the 8 groups: 2,048 workgroups never
-    // serialise on one address.  The last workgroup out redoes the whole queue
-    // if any wave fell back (identical bytes written again), then clears the
-    // scratch for the next launch. ----
-    __shared__ uint32_t last_block;
+    // of each group in one counter for the 8 groups: thousands of workgroups
+    // never serialise on one address.  Bits 0-15 count finished members, the
+    // bits above count members with a wave that did not take its pieces; the
+    // read-modify-write chain on one word carries that to the last workgroup
+    // out without any ordering between words.  The last workgroup then
+    // acquires the finished scan word (all slots visible), redoes the whole
+    // queue if any wave gave up (the same bytes written again), and clears
+    // the scratch for the next launch. ----
+    __shared__ uint32_t gave_up[kBcBlock / 64];
+    __shared__ uint32_t last_block;   // 0, 1 = last, 3 = last and redo the queue
+    if (lane == 0)
+        gave_up[wave_in_block] = sealed ? 0u : 1u;
     __syncthreads();
     if (threadIdx.x == 0) {
+        uint32_t mine = 0;
+#pragma unroll
+        for (int k = 0; k < kBcBlock / 64; k++)
+            mine |= gave_up[k];
         uint32_t last = 0;
         const uint32_t x = blockIdx.x & 7;
-        if (atomic_add_agent(&scr->done_xcd[x].count, 1u) == gridDim.x / 8 - 1) {
+        const uint32_t old = atomic_add_agent(&scr->done_xcd[x].count, 1u | (mine << 16));
+        if ((old & 0xffffu) == gridDim.x / 8 - 1) {
             atomic_store_agent(&scr->done_xcd[x].count, 0u);
-            last = atomic_add_agent(&scr->done_all.count, 1u) == 7 ? 1u : 0u;
+            const uint32_t group = ((old >> 16) | mine) != 0 ? 1u : 0u;
+            const uint32_t old_all = atomic_add_agent(&scr->done_all.count, 1u | (group << 16));
+            if ((old_all & 0xffffu) == 7)
+                last = ((old_all >> 16) | group) != 0 ? 3u : 1u;
         }
         last_block = last;
     }
     __syncthreads();
     if (last_block) {
-        uint32_t q = __builtin_amdgcn_readfirstlane(atomic_load_agent(&scr->qtail.count));
-        if (q > kBcQueueCap)
-            q = kBcQueueCap;
-        if (__builtin_amdgcn_readfirstlane(atomic_load_agent(&scr->fallback.count)) != 0) {
-            for (uint32_t e = threadIdx.x >> 6; e < q; e += kBcBlock / 64) {
-                const uint32_t v = __builtin_amdgcn_readfirstlane(atomic_load_agent(&scr->slot[e]));
-                if (v != 0)
+        // Every scanner counted itself in the scan word before its workgroup
+        // was counted above, so the word is final; the waits below only cover
+        // the visibility of stores that have already been made, and are
+        // bounded all the same (about 10 ms).
+        const uint64_t deadline = (uint64_t)wall_clock64() + 8 * wait_ticks + 1000000u;
+        uint64_t sw = 0;
+        for (;;) {
+            sw = readfirstlane_u64(__hip_atomic_load(&scr->scan.word, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT));
+            if ((uint32_t)(sw >> 32) >= scanners || (uint64_t)wall_clock64() > deadline)
+                break;
+            __builtin_amdgcn_s_sleep(4);
+        }
+        const uint32_t qn = (uint32_t)sw < kBcQueueCap ? (uint32_t)sw : kBcQueueCap;
+        if (last_block == 3u) {
+            for (uint32_t e = wave_in_block; e < qn; e += kBcBlock / 64) {
+                // slot e was claimed, so its scanner has written it
+                uint32_t v;
+                for (;;) {
+                    v = __builtin_amdgcn_readfirstlane(atomic_load_agent(&scr->slot[e]));
+                    if (v != 0 || (uint64_t)wall_clock64() > deadline)
+                        break;
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                if (slot_valid(v, n))
                     wave_copy_any(readfirstlane_u64(desc[v - 1].src), readfirstlane_u64(desc[v - 1].dst),
                                   readfirstlane_u64(desc[v - 1].bytes), lane);
             }
         }
-        for (uint32_t e = threadIdx.x; e < q; e += kBcBlock)
+        __syncthreads();   // every wave has read its slots before any is cleared
+        for (uint32_t e = threadIdx.x; e < qn; e += kBcBlock)
             atomic_store_agent(&scr->slot[e], 0u);
         __syncthreads();
         if (threadIdx.x == 0) {
-            atomic_store_agent(&scr->qtail.count, 0u);
-            atomic_store_agent(&scr->scan_done.count, 0u);
-            atomic_store_agent(&scr->fallback.count, 0u);
+            atomic_store_agent(&scr->scan.word, 0ull);
             atomic_store_agent(&scr->done_all.count, 0u);
         }
     }
@@ -661,13 +720,13 @@ uint32_t batched_scanners(uint32_t ncopies, int grid) {
 }
 
 hipError_t launch_batched_copy(const tb_copy_desc *desc, uint32_t n, BcScratch *scratch, int cu_count,
-                               uint64_t wait_ticks, hipStream_t s) {
+                               uint64_t wait_ticks, bool no_pieces, hipStream_t s) {
     const int grid = batched_grid(n, cu_count);
     // pieces of long copies go to the waves resident from the start: CUs x 8
     // waves per SIMD x 4 SIMDs at most
     const uint32_t resident = (uint32_t)(cu_count > 0 ? cu_count : 1) * kBcResidentWavesPerCu;
     hipLaunchKernelGGL(bc_kernel, dim3(grid), dim3(kBcBlock), 0, s, desc, n, scratch,
-                       batched_scanners(n, grid), wait_ticks, resident);
+                       batched_scanners(n, grid), wait_ticks, resident, no_pieces ? 1u : 0u);
     return hipGetLastError();
 }
 

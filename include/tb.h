@@ -191,6 +191,23 @@ int tb_reduce_copy_ex(float *dst, const float *const *srcs, int32_t nsrc,
 int tb_batched_copy(const tb_copy_desc *desc_dev, uint32_t ncopies, void *stream);
 
 /*
+ * Test hook for the batched copy's recovery path (process-wide; affects
+ * launches made after the call).  Long copies go through a queue whose pieces
+ * the waves share once every scanning workgroup has published; the wait for
+ * that is bounded, and a wave that gives up leaves the queue to the last
+ * workgroup to finish, which copies all of it again.  Modes:
+ *   TB_BC_NORMAL     waves wait up to 200 us of device time (the default);
+ *   TB_BC_NO_WAIT    waves do not wait: any that find the queue unfinished
+ *                    give up;
+ *   TB_BC_LAST_ONLY  every wave gives up: the last workgroup copies the
+ *                    whole queue.
+ * The bytes written are identical in every mode; only the speed differs.
+ * Errors: TB_ERR_INVALID for an unknown mode.
+ */
+enum { TB_BC_NORMAL = 0, TB_BC_NO_WAIT = 1, TB_BC_LAST_ONLY = 2 };
+int tb_batched_set_mode(int32_t mode);
+
+/*
  * Timing gate (nvbandwidth's spin kernel, "nvbandwidth deep dive" §3.3.1):
  * tb_spin_gate_arm enqueues on `stream` a one-thread kernel that waits until
  * tb_spin_gate_release() is called, so that work queued behind it starts back

@@ -36,7 +36,23 @@ def _run_batch(torch, batch: wl.Batch, src_shift: int = 0, dst_shift: int = 0, s
     d[:, 0] += np.uint64(src_shift)
     d[:, 1] += np.uint64(dst_shift)
     oracle.ref_batch(exp, image, d)
-    return oracle.first_mismatch(got, exp)
+    first = oracle.first_mismatch(got, exp)
+    if first != -1:
+        _describe_mismatch(got, exp, d)
+    return first
+
+
+def _describe_mismatch(got, exp, desc):
+    """Print which copies differ and how (not written at all, or partly)."""
+    bad = []
+    for k, (s, dd, b) in enumerate(desc.astype(np.int64)):
+        if b and not np.array_equal(got[dd:dd + b], exp[dd:dd + b]):
+            wrong = np.flatnonzero(got[dd:dd + b] != exp[dd:dd + b])
+            bad.append((k, int(s), int(dd), int(b), len(wrong), int(wrong[0]), int(wrong[-1]),
+                        bool(np.all(got[dd:dd + b][wrong] == wl.POOL_FILL))))
+    note(f"  {len(bad)} copies differ (index, src, dst, bytes, n_wrong, first, last, all_unwritten):")
+    for row in bad[:12]:
+        note(f"    {row}")
 
 
 @pytest.mark.parametrize("seed", range(40))
@@ -103,7 +119,7 @@ def test_large_copies_split_and_queue_reset_across_launches():
 
 def test_queue_overflow_runs_on_owner_waves():
     """More long copies than the queue holds: the overflow ones are copied by
-    the wave that owns them."""
+    the scanning wave that found them."""
     torch = require_gpu()
     rng = np.random.default_rng(9)
     n = 16384 + 300
@@ -115,6 +131,66 @@ def test_queue_overflow_runs_on_owner_waves():
     batch = wl.Batch("overflow", desc, n * size, n * (size + 64), 9, payload=wl.random_payload(rng, n * size))
     note(f"batched queue overflow n={n} size={size}")
     assert _run_batch(torch, batch, launches=2) == -1
+
+
+def _long_and_short_batch(seed: int) -> wl.Batch:
+    """300 long copies (64 KiB + 16 B to 1 MiB, some unaligned) among 1,700
+    short ones, shuffled."""
+    rng = np.random.default_rng(seed)
+    long_sizes = rng.integers(64 * KiB + 1, 1 * MiB, size=300)
+    short_sizes = rng.integers(1, 8 * KiB, size=1700)
+    sizes = np.concatenate([long_sizes, short_sizes]).astype(np.int64)
+    rng.shuffle(sizes)
+    n = len(sizes)
+    gaps_s = rng.integers(0, 48, size=n)
+    gaps_d = rng.integers(0, 48, size=n)
+    src_off = np.concatenate([[0], np.cumsum(sizes[:-1] + gaps_s[:-1])]).astype(np.int64)
+    dst_off = np.concatenate([[0], np.cumsum(sizes[:-1] + gaps_d[:-1])]).astype(np.int64)
+    desc = np.stack([src_off, dst_off, sizes], axis=1).astype(np.uint64)
+    src_total = int(src_off[-1] + sizes[-1])
+    pool = int(dst_off[-1] + sizes[-1]) + 64
+    return wl.Batch(f"long_short_{seed}", desc, src_total, pool, seed, payload=wl.random_payload(rng, src_total))
+
+
+def test_same_batch_moved_by_three_bytes_between_calls():
+    """The same descriptor indices at new addresses: a launch must read the
+    descriptors of its own call, never ones left from the previous call."""
+    torch = require_gpu()
+    batch = _long_and_short_batch(12)
+    note("batched long/short shift 3 then 0")
+    assert _run_batch(torch, batch, src_shift=3, dst_shift=3, launches=2) == -1
+    assert _run_batch(torch, batch, launches=1) == -1
+
+
+@pytest.mark.parametrize("mode", ["TB_BC_NO_WAIT", "TB_BC_LAST_ONLY"])
+@pytest.mark.parametrize("case", ["long_short", "c5_256MiB_pool", "overflow"])
+def test_recovery_path_gives_identical_bytes(mode, case):
+    """Waves that do not wait for the long-copy queue leave it to the last
+    workgroup, which copies every queued copy: the bytes are the oracle's all
+    the same, and a normal launch afterwards finds the scratch cleared."""
+    torch = require_gpu()
+    import copy_reduce_amd as tb
+    if case == "long_short":
+        batch = _long_and_short_batch(12)
+    elif case == "c5_256MiB_pool":
+        batch = wl.batch_c5(pool_bytes=256 * MiB)
+    else:
+        rng = np.random.default_rng(13)
+        n, size = 16384 + 40, 64 * KiB + 16
+        sizes = np.full(n, size, np.int64)
+        src_off = np.arange(n, dtype=np.int64) * size
+        dst_off = rng.permutation(n).astype(np.int64) * (size + 64)
+        desc = np.stack([src_off, dst_off, sizes], axis=1).astype(np.uint64)
+        batch = wl.Batch("overflow", desc, n * size, n * (size + 64), 13, payload=wl.random_payload(rng, n * size))
+    note(f"batched recovery mode={mode} case={case} n={batch.ncopies}")
+    tb.tb_batched_set_mode(getattr(tb, mode))
+    try:
+        assert _run_batch(torch, batch, src_shift=3, dst_shift=3, launches=2) == -1
+        assert _run_batch(torch, batch, launches=1) == -1
+    finally:
+        tb.tb_batched_set_mode(tb.TB_BC_NORMAL)
+    note(f"batched recovery mode={mode} case={case}: normal launch after")
+    assert _run_batch(torch, batch, launches=1) == -1
 
 
 def test_zero_length_and_empty_batches():

@@ -171,6 +171,13 @@ def test_batched_copy_argument_checks():
     assert _st("tb_batched_copy", None, 0, None) == tb.TB_OK
 
 
+def test_batched_mode_hook_checks():
+    for bad in (-1, 3, 1 << 20):
+        assert _st("tb_batched_set_mode", bad) == tb.TB_ERR_INVALID
+    for good in (tb.TB_BC_NO_WAIT, tb.TB_BC_LAST_ONLY, tb.TB_BC_NORMAL):   # ends in the default
+        assert _st("tb_batched_set_mode", good) == tb.TB_OK
+
+
 def test_prep_sources_and_gate_argument_checks():
     assert _st("tb_prep_sources", 0x1000, 64, 0, 0x2000, 16, None) == tb.TB_ERR_INVALID    # k == 0
     assert _st("tb_prep_sources", 0x1000, 32, 2, 0x2000, 16, None) == tb.TB_ERR_INVALID    # stride < bytes
