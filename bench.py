@@ -79,6 +79,27 @@ class Timed:
         return ms, evs[0].elapsed_time(evs[-1]), wall
 
 
+def device_record(torch, tb):
+    """Name, CU count and the partition modes the measurement ran under (the
+    cache behaviour rotation guards against depends on them)."""
+    import glob
+    props = torch.cuda.get_device_properties(0)
+    rec = {"name": props.name or torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", ""),
+           "cu_count": tb.tb_launch_info()["cu_count"],
+           "hbm_bytes": int(props.total_memory)}
+    for key, fname in (("compute_partition", "current_compute_partition"),
+                       ("memory_partition", "current_memory_partition")):
+        vals = set()
+        for path in glob.glob(f"/sys/class/drm/card*/device/{fname}"):
+            try:
+                with open(path) as f:
+                    vals.add(f.read().strip())
+            except OSError:
+                pass
+        rec[key] = "/".join(sorted(vals)) if vals else "unknown"
+    return rec
+
+
 # ---------------------------------------------------------------------------
 # workload set-up (untimed)
 # ---------------------------------------------------------------------------
@@ -181,6 +202,7 @@ def main_line(args, torch, tb, wl):
                              "bytes_per_launch": bc_bytes, "replicas": b["kb"]},
             "launch": info,
         },
+        "device": device_record(torch, tb),
         "parts": {
             "reduce_copy": {"ms_mean": round(rc_mean, 5), "ms_min": round(min(rc_ms), 5),
                             "ms_max": round(max(rc_ms), 5), "gbps": round(rc_gbps, 1),
@@ -278,9 +300,13 @@ def suite(args, torch, tb, wl):
                 return dbase
             return tb.tb_rotate_sources([dbase], rs.stride, kd, i)[0]
 
+        # cold: the first launch after prep, timed on its own (a diagnostic;
+        # the figure is the warm mean below)
+        i0 = -args.warmup if args.warmup else 0
+        cold_ms, _, _ = timer.run([lambda p=rs.pointers(i0), dp=dptr_for(i0): tb.tb_reduce_copy(dp, p, w.nfloats, sh)])
         means = []
-        for _ in range(reps):
-            for i in range(-args.warmup, 0):
+        for rep in range(reps):
+            for i in range(-args.warmup + (1 if rep == 0 and args.warmup else 0), 0):
                 tb.tb_reduce_copy(dptr_for(i), rs.pointers(i), w.nfloats, sh)
             launches = []
             for i in range(args.steps):
@@ -293,6 +319,7 @@ def suite(args, torch, tb, wl):
         out = {"config": w.name + ("_dstrot" if rotate_dst else ""), "nsrc": w.nsrc, "nfloats": w.nfloats,
                "k": rs.k, "reps": reps,
                "ms_mean": round(med[0], 5), "ms_min": round(med[1], 5), "ms_max": round(med[2], 5),
+               "ms_cold": round(cold_ms[0], 5),
                "gbps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
                "aggregate_gbps": round(args.steps * w.algorithmic_bytes / (med[3] * 1e-3) / 1e9, 1)}
         del rs, dst, dsts
@@ -301,7 +328,10 @@ def suite(args, torch, tb, wl):
 
     def batch_line(batch, rotate_bytes, tag):
         b = setup_batch(torch, tb, batch, rotate_bytes)
-        for i in range(-args.warmup, 0):
+        i0 = -args.warmup if args.warmup else 0
+        d0 = batch_desc_for(tb, b, i0)
+        cold_ms, _, _ = timer.run([lambda: tb.tb_batched_copy(int(d0.data_ptr()), batch.ncopies, sh)])
+        for i in range(-args.warmup + (1 if args.warmup else 0), 0):
             d = batch_desc_for(tb, b, i)
             tb.tb_batched_copy(int(d.data_ptr()), batch.ncopies, sh)
         launches = []
@@ -313,30 +343,39 @@ def suite(args, torch, tb, wl):
         gbps = batch.algorithmic_bytes / (mean * 1e-3) / 1e9
         out = {"config": f"{batch.name}_{tag}", "ncopies": batch.ncopies, "payload_bytes": batch.total_bytes,
                "replicas": b["kb"], "ms_mean": round(mean, 5), "ms_min": round(min(ms), 5),
-               "ms_max": round(max(ms), 5), "gbps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+               "ms_max": round(max(ms), 5), "ms_cold": round(cold_ms[0], 5), "gbps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
                "copies_per_s": round(batch.ncopies / (mean * 1e-3), 1)}
         del b
         torch.cuda.empty_cache()
         return out
 
-    for name in ("c1_copy_4MiB_rot", "c1_copy_4MiB_norot", "c2_reduce2_256MiB_rot", "c2_reduce2_256MiB_norot",
-                 "c3_reduce4_64MiB_compress"):
-        print(json.dumps({"suite": reduce_line(wl.REDUCE_CONFIGS[name])}), flush=True)
     # controls beyond the pages' method: destination rotated too (R = 1 GiB for C2 so that K > 1)
     c2cold = wl.ReduceWorkload("c2_reduce2_256MiB_R1GiB", 2, 64 << 20, 4 * wl.DEFAULT_ROTATE_BYTES)
-    print(json.dumps({"suite": reduce_line(c2cold)}), flush=True)
-    print(json.dumps({"suite": reduce_line(c2cold, rotate_dst=True)}), flush=True)
-    print(json.dumps({"suite": reduce_line(wl.REDUCE_CONFIGS["c3_reduce4_64MiB_compress"], rotate_dst=True)}), flush=True)
-    c4 = wl.batch_c4()
-    print(json.dumps({"suite": batch_line(c4, wl.DEFAULT_ROTATE_BYTES, "rotated")}), flush=True)
-    print(json.dumps({"suite": batch_line(c4, 0, "control")}), flush=True)
-    del c4
-    c5 = wl.batch_c5()
-    print(json.dumps({"suite": batch_line(c5, wl.DEFAULT_ROTATE_BYTES, "rotated")}), flush=True)
-    del c5
+    c3 = wl.REDUCE_CONFIGS["c3_reduce4_64MiB_compress"]
+    entries = [(name, lambda n=name: reduce_line(wl.REDUCE_CONFIGS[n]))
+               for name in ("c1_copy_4MiB_rot", "c1_copy_4MiB_norot", "c2_reduce2_256MiB_rot",
+                            "c2_reduce2_256MiB_norot", "c3_reduce4_64MiB_compress")]
+    entries += [
+        (c2cold.name, lambda: reduce_line(c2cold)),
+        (c2cold.name + "_dstrot", lambda: reduce_line(c2cold, rotate_dst=True)),
+        (c3.name + "_dstrot", lambda: reduce_line(c3, rotate_dst=True)),
+        ("c4_scatter_47520_rotated", lambda: batch_line(wl.batch_c4(), wl.DEFAULT_ROTATE_BYTES, "rotated")),
+        ("c4_scatter_47520_control", lambda: batch_line(wl.batch_c4(), 0, "control")),
+        ("c5_mixed_kv_11044_rotated", lambda: batch_line(wl.batch_c5(), wl.DEFAULT_ROTATE_BYTES, "rotated")),
+    ]
     for nbytes in wl.SWEEP_BYTES:
         for rot in (True, False):
-            print(json.dumps({"suite": reduce_line(wl.sweep_workload(nbytes, rot), reps=3)}), flush=True)
+            sw = wl.sweep_workload(nbytes, rot)
+            entries.append((sw.name, lambda sw=sw: reduce_line(sw, reps=3)))
+    names = [n for n, _ in entries]
+    only = [n for n in (args.only or "").split(",") if n]
+    unknown = [n for n in only if n not in names]
+    if unknown:
+        raise SystemExit(f"--only: unknown configuration(s) {unknown}; known: {names}")
+    print(json.dumps({"suite_device": device_record(torch, tb)}), flush=True)
+    for name, fn in entries:
+        if not only or name in only:
+            print(json.dumps({"suite": fn()}), flush=True)
 
 
 def calibrate_copy(torch, tb):
@@ -359,6 +398,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--suite", action="store_true", help="also time every configuration (C1-C5, sweep)")
+    ap.add_argument("--only", default="",
+                    help="comma-separated suite configurations to run (implies --suite; the bench line is skipped)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB copy (tb_reduce_copy, one source) 10 times: the known-size "
                          "kernel that scales rocprofv3's FETCH_SIZE / WRITE_SIZE into HBM bytes")
@@ -384,9 +425,11 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(torch, tb)
         return
-    if args.suite:
+    if args.suite or args.only:
         suite(args, torch, tb, wl)
         torch.cuda.empty_cache()
+        if args.only:
+            return
     main_line(args, torch, tb, wl)
 
 
