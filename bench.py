@@ -378,6 +378,143 @@ def suite(args, torch, tb, wl):
             print(json.dumps({"suite": fn()}), flush=True)
 
 
+# ---------------------------------------------------------------------------
+# --baselines: the HIP runtime's own copies on the same inputs
+# ---------------------------------------------------------------------------
+
+HIP_MEMCPY_D2D = 3          # hipMemcpyDeviceToDevice: the runtime copies with a kernel
+HIP_MEMCPY_D2D_NOCU = 1024  # hipMemcpyDeviceToDeviceNoCU: a copy engine (SDMA), no compute units
+
+
+def hip_memcpy_fn():
+    """hipMemcpyAsync of the HIP runtime torch loaded (the one libtb binds to)."""
+    import ctypes
+    import re
+    with open("/proc/self/maps") as f:
+        paths = sorted(set(re.findall(r"(/\S*libamdhip64\.so\S*)", f.read())))
+    if not paths:
+        raise RuntimeError("the HIP runtime is not loaded")
+    paths.sort(key=lambda q: "torch" not in q)
+    fn = ctypes.CDLL(paths[0]).hipMemcpyAsync
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    return fn
+
+
+def percopy_submit(memcpy, srcs, dsts, sizes, kind, stream_handle):
+    """One hipMemcpyAsync per descriptor; returns (seconds spent submitting, OR of the return codes)."""
+    rc = 0
+    t0 = time.perf_counter()
+    for a, d, n in zip(srcs, dsts, sizes):
+        rc |= memcpy(d, a, n, kind, stream_handle)
+    return time.perf_counter() - t0, rc
+
+
+def batch_sample_check(torch, pool, batch):
+    """Every descriptor's first and last 16 bytes, and every 97th descriptor in
+    full, against the payload (the oracle's per-descriptor memcpy, sampled)."""
+    import numpy as np
+
+    import oracle
+    d = batch.desc.astype(np.int64)
+    d = d[d[:, 2] > 0]
+    k16 = np.minimum(np.arange(16)[None, :], d[:, 2][:, None] - 1)      # clipped to short copies
+    ends = np.concatenate([d[:, 1][:, None] + k16, (d[:, 1] + d[:, 2] - 1)[:, None] - k16], axis=1).ravel()
+    srcs = np.concatenate([d[:, 0][:, None] + k16, (d[:, 0] + d[:, 2] - 1)[:, None] - k16], axis=1).ravel()
+    got = pool[torch.from_numpy(ends).to(pool.device)].cpu().numpy()
+    if oracle.first_mismatch(got, batch.payload[srcs]) != -1:
+        return False
+    for k in range(0, len(d), 97):
+        s0, d0, n0 = (int(x) for x in d[k])
+        if oracle.first_mismatch(pool[d0:d0 + n0].cpu().numpy(), batch.payload[s0:s0 + n0]) != -1:
+            return False
+    return True
+
+
+def baselines(args, torch, tb, wl):
+    """The runtime's device-to-device copy (kernel, and copy engine) on the N = 1
+    configurations, and one hipMemcpyAsync per descriptor for the batched ones:
+    the per-call path a batched kernel replaces (Mooncake RFC #5041, Motivation)."""
+    import numpy as np
+
+    import oracle
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    timer = Timed(torch, tb, stream)
+    memcpy = hip_memcpy_fn()
+    kinds = ((HIP_MEMCPY_D2D, "hipMemcpyAsync D2D (runtime copy kernel)"),
+             (HIP_MEMCPY_D2D_NOCU, "hipMemcpyAsync D2D NoCU (copy engine)"))
+    print(json.dumps({"baseline_device": device_record(torch, tb)}), flush=True)
+
+    def copy_line(w, kind, label, reps):
+        rs, dst = setup_reduce(torch, w)
+        nbytes = w.nfloats * 4
+        dp = int(dst.data_ptr())
+
+        def one(i):
+            (p,) = rs.pointers(i)
+            if memcpy(dp, p, nbytes, kind, sh) != 0:
+                raise RuntimeError(f"hipMemcpyAsync failed ({label})")
+        means = []
+        for rep in range(reps):
+            for i in range(-args.warmup, 0):
+                one(i)
+            ms, _, _ = timer.run([lambda i=i: one(i) for i in range(args.steps)])
+            means.append((statistics.mean(ms), min(ms), max(ms)))
+        med = sorted(means)[len(means) // 2]
+        ok = oracle.first_mismatch(dst.cpu().numpy(), oracle.gen_source(w.nfloats, 0, w.fill)) == -1
+        gbps = w.algorithmic_bytes / (med[0] * 1e-3) / 1e9
+        out = {"config": w.name, "method": label, "k": rs.k, "reps": reps, "ms_mean": round(med[0], 5),
+               "ms_min": round(med[1], 5), "ms_max": round(med[2], 5), "gbps": round(gbps, 1),
+               "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4), "validated": ok}
+        del rs, dst
+        torch.cuda.empty_cache()
+        return out
+
+    def percopy_line(batch, kind, label, runs=3):
+        b = setup_batch(torch, tb, batch, wl.DEFAULT_ROTATE_BYTES)
+        pool_base = int(b["pool"].data_ptr())
+        dsts = (batch.desc[:, 1].astype(np.int64) + pool_base).tolist()
+        sizes = batch.desc[:, 2].astype(np.int64).tolist()
+        srcs_per = [(batch.desc[:, 0].astype(np.int64) + b["base"] + r * b["stride"]).tolist() for r in range(b["kb"])]
+        walls, submits = [], []
+        for i in range(-1, runs):
+            r = oracle.slice_of(i, b["kb"])
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            sub, rc = percopy_submit(memcpy, srcs_per[r], dsts, sizes, kind, sh)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+            if rc != 0:
+                raise RuntimeError(f"hipMemcpyAsync failed ({label})")
+            if i >= 0:
+                walls.append(wall)
+                submits.append(sub)
+        wall, sub = statistics.median(walls), statistics.median(submits)
+        gbps = batch.algorithmic_bytes / wall / 1e9
+        out = {"config": batch.name, "method": label, "calls": batch.ncopies, "replicas": b["kb"], "runs": runs,
+               "wall_ms": round(wall * 1e3, 3), "host_submit_us_per_call": round(sub / batch.ncopies * 1e6, 3),
+               "gbps": round(gbps, 2), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 5),
+               "copies_per_s": round(batch.ncopies / wall, 1),
+               "validated_sample": batch_sample_check(torch, b["pool"], batch)}
+        del b
+        torch.cuda.empty_cache()
+        return out
+
+    for name in ("c1_copy_4MiB_rot", "c1_copy_4MiB_norot"):
+        for kind, label in kinds:
+            print(json.dumps({"baseline": copy_line(wl.REDUCE_CONFIGS[name], kind, label, 1)}), flush=True)
+    for nbytes in wl.SWEEP_BYTES:
+        for rot in (True, False):
+            for kind, label in kinds:
+                print(json.dumps({"baseline": copy_line(wl.sweep_workload(nbytes, rot), kind, label, 3)}), flush=True)
+    for make in (wl.batch_c4, wl.batch_c5):
+        batch = make()
+        for kind, label in kinds:
+            print(json.dumps({"baseline": percopy_line(batch, kind, "one " + label + " per descriptor")}), flush=True)
+        del batch
+
+
 def calibrate_copy(torch, tb):
     """A plain copy of exactly 268,435,456 bytes read and 268,435,456 written per launch."""
     nbytes = 256 << 20
@@ -398,6 +535,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--suite", action="store_true", help="also time every configuration (C1-C5, sweep)")
+    ap.add_argument("--baselines", action="store_true",
+                    help="only time the HIP runtime's own copies (copy kernel, copy engine, one call per "
+                         "descriptor) on the same inputs, then exit")
     ap.add_argument("--only", default="",
                     help="comma-separated suite configurations to run (implies --suite; the bench line is skipped)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -424,6 +564,9 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy(torch, tb)
+        return
+    if args.baselines:
+        baselines(args, torch, tb, wl)
         return
     if args.suite or args.only:
         suite(args, torch, tb, wl)
