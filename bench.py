@@ -515,6 +515,63 @@ def baselines(args, torch, tb, wl):
         del batch
 
 
+# ---------------------------------------------------------------------------
+# --cache-study: what rotation defeats, and what it does not
+# ---------------------------------------------------------------------------
+
+def cache_study(args, torch, tb, wl):
+    """Per size and SRC_ROTATE_BYTES in {0, 256 MiB, 512 MiB, 1 GiB}: the first
+    launch after preparation (cold), the warm mean, and the warm mean with an
+    untimed 1 GiB streaming copy before every launch (memory-side cache flushed;
+    a labelled variant, not the pages' method).  TransferBench PR #365, Test
+    Result and Technical Details."""
+    import oracle
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    timer = Timed(torch, tb, stream)
+    MiB = 1 << 20
+    fa = torch.empty(128 * MiB, dtype=torch.float32, device="cuda")   # 512 MiB each: a 1 GiB flush copy
+    fb = torch.empty_like(fa)
+    fa_p, fb_p = int(fa.data_ptr()), int(fb.data_ptr())
+
+    def flush():
+        tb.tb_reduce_copy(fb_p, [fa_p], fa.numel(), sh)
+
+    print(json.dumps({"cache_study_device": device_record(torch, tb)}), flush=True)
+    shapes = [("copy", 1, 4 * MiB), ("copy", 1, 16 * MiB), ("copy", 1, 64 * MiB), ("reduce2", 2, 256 * MiB),
+              ("copy", 1, 512 * MiB)]
+    for kind, nsrc, nbytes in shapes:
+        for r_mib in (0, 256, 512, 1024):
+            w = wl.ReduceWorkload(f"{kind}_{nbytes // MiB}MiB_R{r_mib}MiB", nsrc, nbytes // 4, r_mib * MiB)
+            rs, dst = setup_reduce(torch, w)
+            dp = int(dst.data_ptr())
+            i0 = -args.warmup if args.warmup else 0
+            cold, _, _ = timer.run([lambda p=rs.pointers(i0): tb.tb_reduce_copy(dp, p, w.nfloats, sh)])
+            for i in range(i0 + 1, 0):
+                tb.tb_reduce_copy(dp, rs.pointers(i), w.nfloats, sh)
+            warm, _, _ = timer.run([lambda p=rs.pointers(i): tb.tb_reduce_copy(dp, p, w.nfloats, sh)
+                                    for i in range(args.steps)])
+            # flushed: events bracket only the measured launch
+            flushed = []
+            for i in range(args.steps):
+                flush()
+                ms, _, _ = timer.run([lambda p=rs.pointers(i): tb.tb_reduce_copy(dp, p, w.nfloats, sh)])
+                flushed.append(ms[0])
+            ok = oracle.first_mismatch(dst.cpu().numpy(), oracle.ref_reduce(
+                [oracle.gen_source(w.nfloats, b, None) for b in range(nsrc)])) == -1
+            wm, fm = statistics.mean(warm), statistics.mean(flushed)
+            gb = w.algorithmic_bytes / 1e9
+            print(json.dumps({"cache_study": {
+                "config": w.name, "nsrc": nsrc, "bytes_per_buffer": nbytes, "rotate_bytes": r_mib * MiB, "k": rs.k,
+                "cold_us": round(cold[0] * 1e3, 2), "warm_us": round(wm * 1e3, 2), "flushed_us": round(fm * 1e3, 2),
+                "cold_frac": round(gb / (cold[0] * 1e-3) / HBM_PEAK_GBPS, 4),
+                "warm_frac": round(gb / (wm * 1e-3) / HBM_PEAK_GBPS, 4),
+                "flushed_frac": round(gb / (fm * 1e-3) / HBM_PEAK_GBPS, 4),
+                "warm_over_cold": round(cold[0] / wm, 3), "validated": ok}}), flush=True)
+            del rs, dst
+            torch.cuda.empty_cache()
+
+
 def calibrate_copy(torch, tb):
     """A plain copy of exactly 268,435,456 bytes read and 268,435,456 written per launch."""
     nbytes = 256 << 20
@@ -538,6 +595,8 @@ def main():
     ap.add_argument("--baselines", action="store_true",
                     help="only time the HIP runtime's own copies (copy kernel, copy engine, one call per "
                          "descriptor) on the same inputs, then exit")
+    ap.add_argument("--cache-study", action="store_true",
+                    help="only run the rotation / cold / warm / flushed study over sizes and SRC_ROTATE_BYTES, then exit")
     ap.add_argument("--only", default="",
                     help="comma-separated suite configurations to run (implies --suite; the bench line is skipped)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -567,6 +626,9 @@ def main():
         return
     if args.baselines:
         baselines(args, torch, tb, wl)
+        return
+    if args.cache_study:
+        cache_study(args, torch, tb, wl)
         return
     if args.suite or args.only:
         suite(args, torch, tb, wl)
