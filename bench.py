@@ -572,6 +572,51 @@ def cache_study(args, torch, tb, wl):
             torch.cuda.empty_cache()
 
 
+# ---------------------------------------------------------------------------
+# --roofs: what this chip's HBM sustains for reads, writes and their mix
+# ---------------------------------------------------------------------------
+
+def roofs(args, torch, tb, wl):
+    """Streams larger than the 256 MB memory-side cache: through the library,
+    a 1 GiB memset (nsrc = 0, writes only), a 16-source reduce of 64 MiB each
+    (reads 94% of the bytes) and a 512 MiB copy (half and half); for
+    reference, torch's own fill kernel over 1 GiB."""
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    timer = Timed(torch, tb, stream)
+    MiB = 1 << 20
+    print(json.dumps({"roof_device": device_record(torch, tb)}), flush=True)
+
+    def timed(label, fn, nbytes, reads, writes):
+        for _ in range(args.warmup):
+            fn()
+        ms, _, _ = timer.run([fn] * args.steps)
+        m = statistics.mean(ms)
+        gbps = nbytes / (m * 1e-3) / 1e9
+        print(json.dumps({"roof": {"stream": label, "bytes_read": reads, "bytes_written": writes,
+                                   "us_mean": round(m * 1e3, 2), "gbps": round(gbps, 1),
+                                   "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}}), flush=True)
+
+    big = torch.empty(256 * MiB, dtype=torch.float32, device="cuda")           # 1 GiB
+    bp = int(big.data_ptr())
+    timed("writes only: tb_reduce_copy nsrc=0, 1 GiB", lambda: tb.tb_reduce_copy(bp, [], big.numel(), sh, 0x5A),
+          1 << 30, 0, 1 << 30)
+    timed("writes only: torch fill_ (its own kernel), 1 GiB", lambda: big.view(torch.uint8).fill_(0x5A),
+          1 << 30, 0, 1 << 30)
+    srcs = [torch.full((16 * MiB,), float(k), dtype=torch.float32, device="cuda") for k in range(16)]   # 64 MiB each
+    dst = torch.empty(16 * MiB, dtype=torch.float32, device="cuda")
+    ptrs = [int(t.data_ptr()) for t in srcs]
+    dp = int(dst.data_ptr())
+    timed("reads 94%: tb_reduce_copy nsrc=16, 64 MiB each", lambda: tb.tb_reduce_copy(dp, ptrs, dst.numel(), sh),
+          17 * 64 * MiB, 16 * 64 * MiB, 64 * MiB)
+    del srcs, dst
+    a = big[:128 * MiB]
+    b = big[128 * MiB:]
+    ap, bp2 = int(a.data_ptr()), int(b.data_ptr())
+    timed("copy: tb_reduce_copy nsrc=1, 512 MiB", lambda: tb.tb_reduce_copy(bp2, [ap], a.numel(), sh),
+          1 << 30, 512 * MiB, 512 * MiB)
+
+
 def calibrate_copy(torch, tb):
     """A plain copy of exactly 268,435,456 bytes read and 268,435,456 written per launch."""
     nbytes = 256 << 20
@@ -595,6 +640,8 @@ def main():
     ap.add_argument("--baselines", action="store_true",
                     help="only time the HIP runtime's own copies (copy kernel, copy engine, one call per "
                          "descriptor) on the same inputs, then exit")
+    ap.add_argument("--roofs", action="store_true",
+                    help="only time write-only, read-mostly and copy streams larger than the memory-side cache, then exit")
     ap.add_argument("--cache-study", action="store_true",
                     help="only run the rotation / cold / warm / flushed study over sizes and SRC_ROTATE_BYTES, then exit")
     ap.add_argument("--only", default="",
@@ -629,6 +676,9 @@ def main():
         return
     if args.cache_study:
         cache_study(args, torch, tb, wl)
+        return
+    if args.roofs:
+        roofs(args, torch, tb, wl)
         return
     if args.suite or args.only:
         suite(args, torch, tb, wl)
