@@ -344,17 +344,27 @@ int tb_shutdown(void) {
     std::lock_guard<std::mutex> lk(g_mu);
     if (g_scratch.empty() && g_gate == nullptr)
         return TB_OK;
-    hipError_t e = hipDeviceSynchronize();
-    if (e != hipSuccess)
-        return hip_fail(e, "hipDeviceSynchronize");
     int current = 0;
-    (void)hipGetDevice(&current);
+    hipError_t e = hipGetDevice(&current);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    // every device that holds scratch finishes its work before the scratch goes
     for (auto &kv : g_scratch) {
-        (void)hipSetDevice(kv.first.first);
+        e = hipSetDevice(kv.first.first);
+        if (e == hipSuccess)
+            e = hipDeviceSynchronize();
+        if (e != hipSuccess) {
+            (void)hipSetDevice(current);
+            return hip_fail(e, "hipDeviceSynchronize");
+        }
         (void)hipFree(kv.second);
     }
-    (void)hipSetDevice(current);
     g_scratch.clear();
+    e = hipSetDevice(current);
+    if (e == hipSuccess)
+        e = hipDeviceSynchronize();   // the spin gate's device
+    if (e != hipSuccess)
+        return hip_fail(e, "hipDeviceSynchronize");
     if (g_gate != nullptr) {
         (void)hipHostFree(g_gate);
         g_gate = nullptr;

@@ -70,12 +70,15 @@ class RotatedSources:
 def reduce_copy(dst, srcs, nfloats: Optional[int] = None, stream: Optional[torch.cuda.Stream] = None,
                 memset_byte: int = 0) -> None:
     """dst = srcs[0] + ... (fixed order) via tb_reduce_copy; tensors or device addresses."""
-    if nfloats is None:
-        if not isinstance(dst, torch.Tensor):
-            raise ValueError("nfloats is required with raw addresses")
+    if isinstance(dst, torch.Tensor):
         if dst.dtype != torch.float32 or not dst.is_cuda or not dst.is_contiguous():
             raise ValueError("dst must be a contiguous float32 CUDA tensor")
-        nfloats = dst.numel()
+        if nfloats is None:
+            nfloats = dst.numel()
+        elif nfloats > dst.numel():
+            raise ValueError("nfloats exceeds dst")
+    elif nfloats is None:
+        raise ValueError("nfloats is required with raw addresses")
     for s in srcs:
         if isinstance(s, torch.Tensor) and (s.dtype != torch.float32 or not s.is_cuda or s.numel() < nfloats):
             raise ValueError("sources must be float32 CUDA tensors of at least nfloats elements")
@@ -95,7 +98,10 @@ def make_desc(offsets: np.ndarray, src_base: int, dst_base: int, device=None) ->
 def batched_copy(desc: torch.Tensor, ncopies: Optional[int] = None,
                  stream: Optional[torch.cuda.Stream] = None) -> None:
     """tb_batched_copy over a device (n, 3) int64 descriptor tensor."""
-    if desc.dtype != torch.int64 or not desc.is_cuda or not desc.is_contiguous():
+    if (desc.dtype != torch.int64 or not desc.is_cuda or not desc.is_contiguous() or desc.dim() != 2
+            or desc.shape[1] != 3):
         raise ValueError("desc must be a contiguous int64 CUDA tensor of shape (n, 3)")
     n = desc.shape[0] if ncopies is None else ncopies
+    if not 0 <= n <= desc.shape[0]:
+        raise ValueError("ncopies must be between 0 and the number of descriptors in desc")
     _tb.tb_batched_copy(desc.data_ptr(), n, stream_handle(stream))

@@ -220,3 +220,24 @@ def test_two_streams_use_separate_scratch():
     assert _run_batch(torch, batch, stream=s1) == -1
     note("batched on stream 2")
     assert _run_batch(torch, batch, stream=s2) == -1
+
+
+def test_torch_conveniences_reject_out_of_range_counts():
+    """The torch wrappers refuse counts beyond the tensors they were given, so
+    no launch can read or write past them."""
+    torch = require_gpu()
+    from copy_reduce_amd.torch_api import batched_copy, reduce_copy
+    desc = torch.zeros((4, 3), dtype=torch.int64, device="cuda")
+    with pytest.raises(ValueError):
+        batched_copy(desc, ncopies=5)
+    with pytest.raises(ValueError):
+        batched_copy(desc.view(-1))
+    dst = torch.zeros(100, dtype=torch.float32, device="cuda")
+    src = torch.zeros(200, dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        reduce_copy(dst, [src], nfloats=101)
+    with pytest.raises(ValueError):
+        reduce_copy(dst, [src[:50]])
+    reduce_copy(dst, [src], nfloats=100)
+    batched_copy(desc, ncopies=0)
+    torch.cuda.synchronize()
