@@ -573,6 +573,112 @@ def cache_study(args, torch, tb, wl):
 
 
 # ---------------------------------------------------------------------------
+# --interference: the batched copy beside a GEMM that fills the compute units
+# ---------------------------------------------------------------------------
+
+def interference(args, torch, tb, wl):
+    """A bf16 GEMM stream on a second stream (default priority) while C4 runs:
+    the batched launch and one hipMemcpyAsync per descriptor, each alone and
+    under the GEMM, and the GEMM's own slowdown.  Mooncake RFC #5041
+    (Motivation) reports per-call copies collapsing under such a GEMM."""
+    import numpy as np
+
+    import oracle
+    s_copy = torch.cuda.current_stream()
+    s_gemm = torch.cuda.Stream()
+    sh = s_copy.cuda_stream
+    timer = Timed(torch, tb, s_copy)
+    M = 8192
+    g = torch.Generator(device="cuda").manual_seed(1)
+    A = torch.randn(M, M, dtype=torch.bfloat16, device="cuda", generator=g)
+    B = torch.randn(M, M, dtype=torch.bfloat16, device="cuda", generator=g)
+    C = torch.empty(M, M, dtype=torch.bfloat16, device="cuda")
+    flop = 2.0 * M ** 3
+
+    def gemms(n):
+        """Enqueue n GEMMs on the GEMM stream between two events."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(s_gemm):
+            e0.record(s_gemm)
+            for _ in range(n):
+                torch.mm(A, B, out=C)
+            e1.record(s_gemm)
+        return e0, e1
+
+    with torch.cuda.stream(s_gemm):
+        for _ in range(3):
+            torch.mm(A, B, out=C)
+    torch.cuda.synchronize()
+    e0, e1 = gemms(10)
+    torch.cuda.synchronize()
+    gemm_ms = e0.elapsed_time(e1) / 10
+
+    batch = wl.batch_c4()
+    b = setup_batch(torch, tb, batch, wl.DEFAULT_ROTATE_BYTES)
+
+    def copies():
+        for i in range(-args.warmup, 0):
+            tb.tb_batched_copy(int(batch_desc_for(tb, b, i).data_ptr()), batch.ncopies, sh)
+        ds = [batch_desc_for(tb, b, i) for i in range(args.steps)]
+        ms, _, _ = timer.run([lambda d=d: tb.tb_batched_copy(int(d.data_ptr()), batch.ncopies, sh) for d in ds])
+        return statistics.mean(ms)
+
+    alone_ms = copies()
+    ng = max(4, int(round(4 * alone_ms * (args.steps + args.warmup) / gemm_ms)) + 4)
+    torch.cuda.synchronize()
+    g0, g1 = gemms(ng)
+    under_ms = copies()
+    torch.cuda.synchronize()
+    gemm_under_ms = g0.elapsed_time(g1) / ng
+    ok_batched = batch_sample_check(torch, b["pool"], batch)
+
+    # one hipMemcpyAsync per descriptor, the first 2,000 descriptors of C4
+    memcpy = hip_memcpy_fn()
+    k = 2000
+    pool_base = int(b["pool"].data_ptr())
+    srcs = (batch.desc[:k, 0].astype(np.int64) + b["base"]).tolist()
+    dsts = (batch.desc[:k, 1].astype(np.int64) + pool_base).tolist()
+    sizes = batch.desc[:k, 2].astype(np.int64).tolist()
+    bytes_k = 2 * int(batch.desc[:k, 2].sum())
+
+    def percopy():
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        _, rc = percopy_submit(memcpy, srcs, dsts, sizes, HIP_MEMCPY_D2D, sh)
+        s_copy.synchronize()
+        if rc != 0:
+            raise RuntimeError("hipMemcpyAsync failed")
+        return time.perf_counter() - t0
+
+    percopy()
+    pc_alone = statistics.median([percopy() for _ in range(3)])
+    ng2 = max(4, int(round(pc_alone * 1e3 * 3 / gemm_ms)) + 4)
+    g0, g1 = gemms(ng2)
+    pc_under = statistics.median([percopy() for _ in range(3)])
+    torch.cuda.synchronize()
+    sub = batch.desc[:k]
+    ok_percopy = all(oracle.first_mismatch(b["pool"][int(d):int(d) + int(n)].cpu().numpy(),
+                                           batch.payload[int(s):int(s) + int(n)]) == -1
+                     for s, d, n in sub[::50])
+    rec = {
+        "gemm": {"shape": [M, M, M], "dtype": "bf16", "ms_alone": round(gemm_ms, 4),
+                 "tflops_alone": round(flop / (gemm_ms * 1e-3) / 1e12, 1),
+                 "ms_under_batched_copies": round(gemm_under_ms, 4),
+                 "slowdown": round(gemm_under_ms / gemm_ms, 3)},
+        "batched_copy_c4": {"us_alone": round(alone_ms * 1e3, 2), "us_under_gemm": round(under_ms * 1e3, 2),
+                            "slowdown": round(under_ms / alone_ms, 3),
+                            "gbps_under_gemm": round(batch.algorithmic_bytes / (under_ms * 1e-3) / 1e9, 1),
+                            "validated_sample": ok_batched},
+        "per_call_hipMemcpyAsync_2000_of_c4": {
+            "ms_alone": round(pc_alone * 1e3, 3), "ms_under_gemm": round(pc_under * 1e3, 3),
+            "slowdown": round(pc_under / pc_alone, 3),
+            "gbps_alone": round(bytes_k / pc_alone / 1e9, 3), "gbps_under_gemm": round(bytes_k / pc_under / 1e9, 3),
+            "validated_sample": ok_percopy},
+    }
+    print(json.dumps({"interference": rec}), flush=True)
+
+
+# ---------------------------------------------------------------------------
 # --roofs: what this chip's HBM sustains for reads, writes and their mix
 # ---------------------------------------------------------------------------
 
@@ -640,6 +746,8 @@ def main():
     ap.add_argument("--baselines", action="store_true",
                     help="only time the HIP runtime's own copies (copy kernel, copy engine, one call per "
                          "descriptor) on the same inputs, then exit")
+    ap.add_argument("--interference", action="store_true",
+                    help="only time C4 (batched, and one call per descriptor) alone and beside a bf16 GEMM, then exit")
     ap.add_argument("--roofs", action="store_true",
                     help="only time write-only, read-mostly and copy streams larger than the memory-side cache, then exit")
     ap.add_argument("--cache-study", action="store_true",
@@ -679,6 +787,9 @@ def main():
         return
     if args.roofs:
         roofs(args, torch, tb, wl)
+        return
+    if args.interference:
+        interference(args, torch, tb, wl)
         return
     if args.suite or args.only:
         suite(args, torch, tb, wl)
