@@ -88,6 +88,10 @@ constexpr size_t kBcScratchBytes = sizeof(BcScratch);
 
 int batched_grid(uint32_t ncopies, int cu_count);
 uint32_t batched_scanners(uint32_t ncopies, int grid);
+// Workgroups that take part in the completion count: those holding the
+// piece_waves waves resident from the start, and every scanner; a multiple of
+// 8, at most grid.
+uint32_t batched_counted(uint32_t piece_waves, uint32_t scanners, int grid);
 
 // Enqueue the batched copy.  `scratch` must be kBcScratchBytes of device
 // memory that was zeroed once; the kernel leaves it zeroed again.

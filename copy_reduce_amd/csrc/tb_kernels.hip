@@ -501,7 +501,8 @@ __device__ __forceinline__ bool slot_valid(uint32_t v, uint32_t n) {
 __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_copy_desc *__restrict__ desc,
                                                                       uint32_t n, BcScratch *scr,
                                                                       uint32_t scanners, uint64_t wait_ticks,
-                                                                      uint32_t piece_waves, uint32_t no_pieces) {
+                                                                      uint32_t piece_waves, uint32_t counted,
+                                                                      uint32_t no_pieces) {
     const int lane = threadIdx.x & 63;
     // wave-uniform values kept in scalar registers (readfirstlane tells the
     // compiler so; otherwise their arithmetic would run per lane)
@@ -574,9 +575,12 @@ __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_c
     // g mod P (P = the waves resident from the start), so no atomics are
     // needed to share them.  A wave that gives up waiting, or meets a slot it
     // cannot see yet, leaves the queue to the last workgroup instead. ----
+    // Only the first P waves take pieces; the others never touch the queue.
+    const uint32_t P = piece_waves < W ? piece_waves : W;
+    const bool takes_pieces = wave < P;
     bool sealed = false;
     uint32_t q = 0;
-    if (!no_pieces) {
+    if (takes_pieces && !no_pieces) {
         const uint64_t t0 = wall_clock64();
         for (;;) {
             const uint64_t sw = readfirstlane_u64(atomic_load_agent(&scr->scan.word));
@@ -590,7 +594,6 @@ __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_c
             __builtin_amdgcn_s_sleep(4);
         }
     }
-    const uint32_t P = piece_waves < W ? piece_waves : W;
     if (sealed) {
         uint32_t base_mod = 0;   // (number of the first piece of this group) mod P
         for (uint32_t g0 = 0; g0 < q && sealed; g0 += 64) {
@@ -612,10 +615,7 @@ __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_c
             const uint32_t incl = wave_inclusive_sum(npieces, lane);
             const uint32_t excl = incl - npieces;
             const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
-            // this wave's pieces: g = base + r with g = wave (mod P), for the
-            // first P waves
-            if (wave >= P)
-                break;
+            // this wave's pieces: g = base + r with g = wave (mod P)
             for (uint32_t r = (wave + P - base_mod) % P; r < total; r += P) {
                 const uint64_t owners = __ballot(e < q && excl <= r);
                 const int j = 63 - __builtin_clzll(owners);
@@ -630,20 +630,25 @@ __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_c
         }
     }
 
-    // ---- 4. Completion.  Workgroups count in per-XCD counters (gridDim.x is
-    // a multiple of 8, so each XCD group has gridDim.x / 8 members), the last
-    // of each group in one counter for the 8 groups: thousands of workgroups
-    // never serialise on one address.  Bits 0-15 count finished members, the
+    // ---- 4. Completion, for the first `counted` workgroups only: they hold
+    // every wave that takes pieces and every scanner, so no other workgroup
+    // reads or writes the scratch, and the others leave here.  Counted
+    // workgroups count in per-XCD counters (`counted` is a multiple of 8, so
+    // each XCD group has counted / 8 members), the last of each group in one
+    // counter for the 8 groups: thousands of workgroups never serialise on
+    // one address.  Bits 0-15 count finished members, the
     // bits above count members with a wave that did not take its pieces; the
     // read-modify-write chain on one word carries that to the last workgroup
     // out without any ordering between words.  The last workgroup then
     // acquires the finished scan word (all slots visible), redoes the whole
     // queue if any wave gave up (the same bytes written again), and clears
     // the scratch for the next launch. ----
+    if (blockIdx.x >= counted)
+        return;
     __shared__ uint32_t gave_up[kBcBlock / 64];
     __shared__ uint32_t last_block;   // 0, 1 = last, 3 = last and redo the queue
     if (lane == 0)
-        gave_up[wave_in_block] = sealed ? 0u : 1u;
+        gave_up[wave_in_block] = takes_pieces && !sealed ? 1u : 0u;
     __syncthreads();
     if (threadIdx.x == 0) {
         uint32_t mine = 0;
@@ -653,7 +658,7 @@ __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_c
         uint32_t last = 0;
         const uint32_t x = blockIdx.x & 7;
         const uint32_t old = atomic_add_agent(&scr->done_xcd[x].count, 1u | (mine << 16));
-        if ((old & 0xffffu) == gridDim.x / 8 - 1) {
+        if ((old & 0xffffu) == counted / 8 - 1) {
             atomic_store_agent(&scr->done_xcd[x].count, 0u);
             const uint32_t group = ((old >> 16) | mine) != 0 ? 1u : 0u;
             const uint32_t old_all = atomic_add_agent(&scr->done_all.count, 1u | (group << 16));
@@ -723,14 +728,23 @@ uint32_t batched_scanners(uint32_t ncopies, int grid) {
     return s;
 }
 
+uint32_t batched_counted(uint32_t piece_waves, uint32_t scanners, int grid) {
+    uint32_t c = (piece_waves + kBcBlock / 64 - 1) / (kBcBlock / 64);   // workgroups holding piece waves
+    if (c < scanners)
+        c = scanners;
+    c = (c + 7) & ~7u;
+    return c < (uint32_t)grid ? c : (uint32_t)grid;   // grid is a multiple of 8
+}
+
 hipError_t launch_batched_copy(const tb_copy_desc *desc, uint32_t n, BcScratch *scratch, int cu_count,
                                uint64_t wait_ticks, bool no_pieces, hipStream_t s) {
     const int grid = batched_grid(n, cu_count);
     // pieces of long copies go to the waves resident from the start: CUs x 8
     // waves per SIMD x 4 SIMDs at most
     const uint32_t resident = (uint32_t)(cu_count > 0 ? cu_count : 1) * kBcResidentWavesPerCu;
-    hipLaunchKernelGGL(bc_kernel, dim3(grid), dim3(kBcBlock), 0, s, desc, n, scratch,
-                       batched_scanners(n, grid), wait_ticks, resident, no_pieces ? 1u : 0u);
+    const uint32_t scanners = batched_scanners(n, grid);
+    hipLaunchKernelGGL(bc_kernel, dim3(grid), dim3(kBcBlock), 0, s, desc, n, scratch, scanners, wait_ticks, resident,
+                       batched_counted(resident, scanners, grid), no_pieces ? 1u : 0u);
     return hipGetLastError();
 }
 
