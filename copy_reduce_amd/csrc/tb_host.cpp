@@ -59,11 +59,18 @@ int device_info(DeviceInfo *out) {
     return TB_OK;
 }
 
-// Batched-copy scratch, one per (device, stream), zeroed once at allocation;
-// the kernel leaves it zeroed after every launch.
-std::map<std::pair<int, hipStream_t>, void *> g_scratch;
+// Batched-copy scratch, one per (device, stream), zeroed once at allocation,
+// with the epoch of the last launch made on it (launches on one stream are
+// ordered, which the kernel's reuse of the scratch relies on).
+struct Scratch {
+    void *mem = nullptr;
+    uint64_t epoch = 0;
+};
+std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
 
-int scratch_for(hipStream_t stream, tbk::BcScratch **out) {
+// The scratch for `stream` on the current device, and the epoch of the launch
+// about to be made on it (from 1; 64 bits never wrap in practice).
+int scratch_for(hipStream_t stream, tbk::BcScratch **out, uint64_t *epoch) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
@@ -72,7 +79,10 @@ int scratch_for(hipStream_t stream, tbk::BcScratch **out) {
     auto key = std::make_pair(dev, stream);
     auto it = g_scratch.find(key);
     if (it != g_scratch.end()) {
-        *out = static_cast<tbk::BcScratch *>(it->second);
+        Scratch &sc = it->second;
+        sc.epoch += 1;
+        *out = static_cast<tbk::BcScratch *>(sc.mem);
+        *epoch = sc.epoch;
         return TB_OK;
     }
     void *p = nullptr;
@@ -88,8 +98,12 @@ int scratch_for(hipStream_t stream, tbk::BcScratch **out) {
         (void)hipFree(p);
         return hip_fail(e, "hipMemset(batched-copy scratch)");
     }
-    g_scratch[key] = p;
+    Scratch sc;
+    sc.mem = p;
+    sc.epoch = 1;
+    g_scratch[key] = sc;
     *out = static_cast<tbk::BcScratch *>(p);
+    *epoch = 1;
     return TB_OK;
 }
 
@@ -269,13 +283,14 @@ int tb_batched_copy(const tb_copy_desc *desc_dev, uint32_t ncopies, void *stream
         return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     tbk::BcScratch *scratch = nullptr;
-    rc = scratch_for(s, &scratch);
+    uint64_t epoch = 0;
+    rc = scratch_for(s, &scratch, &epoch);
     if (rc != TB_OK)
         return rc;
     const int mode = g_batched_mode.load(std::memory_order_relaxed);
     const uint64_t wait_ticks =
         mode == TB_BC_NORMAL ? (uint64_t)tbk::kBcSealWaitUs * info.wall_clock_khz / 1000u : 0u;
-    hipError_t e = tbk::launch_batched_copy(desc_dev, ncopies, scratch, info.cu_count, wait_ticks,
+    hipError_t e = tbk::launch_batched_copy(desc_dev, ncopies, scratch, epoch, info.cu_count, wait_ticks,
                                             mode == TB_BC_LAST_ONLY, s);
     if (e != hipSuccess)
         return hip_fail(e, "batched-copy launch");
@@ -357,7 +372,7 @@ int tb_shutdown(void) {
             (void)hipSetDevice(current);
             return hip_fail(e, "hipDeviceSynchronize");
         }
-        (void)hipFree(kv.second);
+        (void)hipFree(kv.second.mem);
     }
     g_scratch.clear();
     e = hipSetDevice(current);

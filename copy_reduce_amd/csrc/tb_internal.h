@@ -41,17 +41,20 @@ hipError_t launch_reduce_copy(const ReduceArgs &args, int nsrc, bool vector_path
 
 constexpr int kBcBlock = 256;        // 4 wave64s per workgroup
 // Occupancy: 7 workgroups (28 waves) per CU is what the kernel reaches at
-// 72 VGPRs without spilling; the waves resident from the start share the
+// 72 VGPRs without spilling; that many waves (the last ones of the grid) share the
 // pieces of long copies.
 constexpr int kBcBlocksPerCu = 7;
 constexpr uint32_t kBcResidentWavesPerCu = kBcBlocksPerCu * (kBcBlock / 64);
 // Launched grid: about kBcDescPerWave descriptors per wave, between the
 // resident count (kBcBlocksPerCu per CU) and kBcMaxGridPerCu per CU.  More
-// workgroups than resident let the dispatcher hand finished CUs new work
-// (+3-5% on the 47,520-copy batch); on small batches extra workgroups only
-// add scan and completion overhead (-9% on the 11,044-copy batch at 16/CU).
-constexpr int kBcMaxGridPerCu = 16;
-constexpr uint32_t kBcDescPerWave = 3;
+// workgroups than resident let the dispatcher hand finished CUs new work:
+// waves own random-size copies and a workgroup's slot is held until its
+// slowest wave is done, so smaller units balance better.  Measured on the
+// 47,520-copy batch: 3, 2, 1.5 and 1 descriptors per wave gave 53%, 55%,
+// 56% and 57% of HBM peak.  No workgroup waits for another at the end, so
+// workgroups past the resident ones cost little.
+constexpr int kBcMaxGridPerCu = 64;
+constexpr uint32_t kBcDescPerWave = 1;
 // Copies longer than this are published in a queue and split into kBcChunk
 // pieces dealt over all waves; shorter ones are copied whole by their owner.
 constexpr uint64_t kBcSplitAbove = 64 * 1024;
@@ -74,31 +77,32 @@ struct alignas(256) BcWord {
     uint64_t pad[31];
 };
 
+// Batched-copy scratch.  Nothing in it is ever cleared after a launch:
+//  - launch e uses scan[e & 1] and clears scan[(e + 1) & 1] for launch e + 1
+//    (launches on one scratch are ordered by their stream);
+//  - a slot carries the epoch e of the launch that wrote it, so a reader tells
+//    a stale slot from a current one;
+//  - redo holds the epoch of the last launch in which a wave took on the
+//    recovery copy.
 struct BcScratch {
-    BcWord scan;            // low 32 bits: queue slots handed out (may exceed
+    BcWord scan[2];         // low 32 bits: queue slots handed out (may exceed
                             // kBcQueueCap); high 32 bits: scanners finished
-    BcCounter done_all;     // bits 0-15: XCD groups finished; above: groups
-                            // with a wave that left the queue to the last one
-    BcCounter done_xcd[8];  // the same per XCD group (blockIdx % 8), counting
-                            // workgroups; at most 65,535 per group
-    uint32_t slot[kBcQueueCap];  // descriptor index + 1 of each queued copy
+    BcWord redo;
+    uint64_t slot[kBcQueueCap];  // (low 32 bits of epoch << 32) | (descriptor index + 1)
 };
 
 constexpr size_t kBcScratchBytes = sizeof(BcScratch);
 
 int batched_grid(uint32_t ncopies, int cu_count);
 uint32_t batched_scanners(uint32_t ncopies, int grid);
-// Workgroups that take part in the completion count: those holding the
-// piece_waves waves resident from the start, and every scanner; a multiple of
-// 8, at most grid.
-uint32_t batched_counted(uint32_t piece_waves, uint32_t scanners, int grid);
 
 // Enqueue the batched copy.  `scratch` must be kBcScratchBytes of device
-// memory that was zeroed once; the kernel leaves it zeroed again.
+// memory that was zeroed once; `epoch` numbers the launches made on it, from
+// 1, one more for each launch (their stream orders them).
 // wait_ticks: the longest wait for the queue, in ticks of the device wall
 // clock (normally kBcSealWaitUs).  no_pieces: no wave takes queue pieces, so
-// the last workgroup copies every queued copy (the recovery path, for tests).
-hipError_t launch_batched_copy(const tb_copy_desc *desc, uint32_t n, BcScratch *scratch,
+// the recovery copy runs (for tests).
+hipError_t launch_batched_copy(const tb_copy_desc *desc, uint32_t n, BcScratch *scratch, uint64_t epoch,
                                int cu_count, uint64_t wait_ticks, bool no_pieces, hipStream_t stream);
 
 // ---- spin gate ---------------------------------------------------------------

@@ -289,18 +289,20 @@ hipError_t launch_reduce_copy(const ReduceArgs &a, int nsrc, bool vector_path, i
 // (Mooncake RFC #5041, Design of #5040: one launch over a (src, dst, len)
 //  descriptor array; 16-byte vectors where the ranges allow.)
 //
-// Persistent grid of 7 to 16 workgroups per CU (about 3 descriptors per
-// wave); the unit of work is a wave64.  Wave w owns descriptors w, w + W,
-// w + 2W, ... (W waves in all) and fetches up to 64 of them with one load per
-// lane.  It broadcasts each to the whole wave (readlane, so addresses and
-// lengths are scalar) and copies it with 16-byte lanes, 8 loads in flight per
-// lane before the matching stores.  Copies longer than kBcSplitAbove instead
-// go through a queue: the first workgroups scan the descriptors and publish
-// them, and once every scanner has finished the queue is cut into kBcChunk
-// pieces dealt round-robin to the resident waves, without atomics.  Every
+// Grid of about one descriptor per wave (between 7 and 64 workgroups per CU);
+// the unit of work is a wave64.  Wave w owns descriptors w, w + W, w + 2W, ...
+// (W waves in all) and fetches up to 64 of them with one load per lane.  It
+// broadcasts each to the whole wave (readlane, so addresses and lengths are
+// scalar) and copies it with 16-byte lanes, 8 loads in flight per lane before
+// the matching stores.  Copies longer than kBcSplitAbove instead go through a
+// queue: the first workgroups scan the descriptors and publish them, and once
+// every scanner has finished the queue is cut into kBcChunk pieces dealt
+// round-robin to the last waves of the grid, without atomics.  Every
 // wait is bounded: a wave that cannot see the finished queue in time leaves
-// its pieces, and the last workgroup to finish then copies the whole queue.
-// That workgroup also clears the scratch for the next launch.
+// its pieces, and the first such wave copies every long copy whole.  No
+// workgroup waits for any other at the end, and nothing in the scratch is
+// cleared after a launch (scan words alternate by launch; slots carry the
+// launch's epoch).
 // ============================================================================
 
 constexpr int kBcUnroll = 8;   // 8 x 16 B x 64 lanes = 8 KiB per wave step
@@ -492,23 +494,49 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x, int lane) {
     return x;
 }
 
-// A queue slot holds descriptor index + 1; 0 (not yet visible) or anything
-// past the batch counts as missing.
-__device__ __forceinline__ bool slot_valid(uint32_t v, uint32_t n) {
-    return v != 0 && v <= n;
+// A queue slot holds (low 32 bits of the epoch << 32) | (descriptor index + 1).
+// It is current when its epoch is this launch's and the index lies in the
+// batch; anything else (not yet visible, or left by an earlier launch) counts
+// as missing.
+__device__ __forceinline__ bool slot_current(uint64_t v, uint64_t epoch, uint32_t n) {
+    const uint32_t idx1 = (uint32_t)v;
+    return (uint32_t)(v >> 32) == (uint32_t)epoch && idx1 != 0 && idx1 <= n;
+}
+
+// Recovery copy: every long copy of the batch, found in the descriptor array
+// itself (not through the queue), copied whole by one wave.  It writes the
+// same bytes as the pieces, so it may overlap them in time.
+__device__ __forceinline__ void copy_all_long(const tb_copy_desc *__restrict__ desc, uint32_t n, int lane) {
+    for (uint64_t b0 = 0; b0 < n; b0 += 64) {
+        const uint64_t i = b0 + lane;
+        const bool is_long = i < n && desc[i].bytes > kBcSplitAbove;
+        uint64_t todo = __ballot(is_long);
+        while (todo) {
+            const int j = __builtin_ctzll(todo);
+            todo &= todo - 1;
+            const uint64_t di = readlane_u64(i, j);
+            wave_copy_any(readfirstlane_u64(desc[di].src), readfirstlane_u64(desc[di].dst),
+                          readfirstlane_u64(desc[di].bytes), lane);
+        }
+    }
 }
 
 __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_copy_desc *__restrict__ desc,
-                                                                      uint32_t n, BcScratch *scr,
+                                                                      uint32_t n, BcScratch *scr, uint64_t epoch,
                                                                       uint32_t scanners, uint64_t wait_ticks,
-                                                                      uint32_t piece_waves, uint32_t counted,
-                                                                      uint32_t no_pieces) {
+                                                                      uint32_t piece_waves, uint32_t no_pieces) {
     const int lane = threadIdx.x & 63;
     // wave-uniform values kept in scalar registers (readfirstlane tells the
     // compiler so; otherwise their arithmetic would run per lane)
     const uint32_t wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t W = gridDim.x * (kBcBlock / 64);
     const uint32_t wave = blockIdx.x * (kBcBlock / 64) + wave_in_block;
+    uint64_t *scan = &scr->scan[epoch & 1].word;
+
+    // The word the next launch on this scratch will use (this launch's was
+    // cleared by the previous one).
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        atomic_store_agent(&scr->scan[(epoch + 1) & 1].word, 0ull);
 
     // ---- 1. The first `scanners` workgroups (dispatched first) find the long
     // copies and publish them.  Slots are claimed on the low half of the scan
@@ -524,9 +552,9 @@ __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_c
             bool here = false;
             if (i < hi && desc[i].bytes > kBcSplitAbove) {
                 // n < 2^32 claims in all, so the low half never carries
-                const uint32_t slot = (uint32_t)atomic_add_agent(&scr->scan.word, 1ull);
+                const uint32_t slot = (uint32_t)atomic_add_agent(scan, 1ull);
                 if (slot < kBcQueueCap)
-                    atomic_store_agent(&scr->slot[slot], (uint32_t)i + 1u);
+                    atomic_store_agent(&scr->slot[slot], (epoch << 32) | (uint32_t)(i + 1));
                 else
                     here = true;
             }
@@ -546,7 +574,7 @@ __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_c
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (threadIdx.x == 0)
-            atomic_add_agent(&scr->scan.word, 1ull << 32);
+            atomic_add_agent(scan, 1ull << 32);
     }
 
     // ---- 2. Own descriptors w, w + W, ...: copy the short ones whole (the
@@ -568,22 +596,26 @@ __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_c
         }
     }
 
-    // ---- 3. Wait (bounded) until every scanner has finished.  The queue
-    // length is then final, and it comes in the same word as the count of
-    // finished scanners, so every wave sees the same length.  The kBcChunk
-    // pieces are numbered across all entries and piece g goes to wave
-    // g mod P (P = the waves resident from the start), so no atomics are
-    // needed to share them.  A wave that gives up waiting, or meets a slot it
-    // cannot see yet, leaves the queue to the last workgroup instead. ----
-    // Only the first P waves take pieces; the others never touch the queue.
+    // ---- 3. The last P waves of the grid share the queue's kBcChunk
+    // pieces; the others are done.  The last ones, not the first: they are
+    // dispatched after the scanners have finished (the first waves would sit
+    // waiting for them, holding their slots, which measured 6 us slower on a
+    // 47,520-copy batch), and P = the waves that fit on the chip at once, so
+    // all of them can run together.  A piece wave waits (bounded) until every
+    // scanner has finished: the queue length is then final, and it comes in
+    // the same word as the count of finished scanners, so every wave sees the
+    // same length.  The pieces are numbered across all entries and piece g
+    // goes to piece wave g mod P, so no atomics are needed to share them. ----
     const uint32_t P = piece_waves < W ? piece_waves : W;
-    const bool takes_pieces = wave < P;
+    if (wave < W - P)
+        return;
+    const uint32_t pw = wave - (W - P);   // piece wave index, in [0, P)
     bool sealed = false;
     uint32_t q = 0;
-    if (takes_pieces && !no_pieces) {
+    if (!no_pieces) {
         const uint64_t t0 = wall_clock64();
         for (;;) {
-            const uint64_t sw = readfirstlane_u64(atomic_load_agent(&scr->scan.word));
+            const uint64_t sw = readfirstlane_u64(atomic_load_agent(scan));
             if ((uint32_t)(sw >> 32) >= scanners) {
                 sealed = true;
                 q = (uint32_t)sw < kBcQueueCap ? (uint32_t)sw : kBcQueueCap;
@@ -596,17 +628,18 @@ __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_c
     }
     if (sealed) {
         uint32_t base_mod = 0;   // (number of the first piece of this group) mod P
-        for (uint32_t g0 = 0; g0 < q && sealed; g0 += 64) {
+        for (uint32_t g0 = 0; g0 < q; g0 += 64) {
             // lane l holds entry g0 + l: its descriptor index and piece count
             const uint32_t e = g0 + lane;
-            uint32_t v = 0, npieces = 0;
+            uint64_t v = 0;
+            uint32_t npieces = 0;
             bool missing = false;
             if (e < q) {
                 v = atomic_load_agent(&scr->slot[e]);
-                if (!slot_valid(v, n))
+                if (!slot_current(v, epoch, n))
                     missing = true;
                 else
-                    npieces = (uint32_t)((desc[v - 1].bytes + kBcChunk - 1) / kBcChunk);
+                    npieces = (uint32_t)((desc[(uint32_t)v - 1].bytes + kBcChunk - 1) / kBcChunk);
             }
             if (__ballot(missing)) {
                 sealed = false;
@@ -615,12 +648,12 @@ __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_c
             const uint32_t incl = wave_inclusive_sum(npieces, lane);
             const uint32_t excl = incl - npieces;
             const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
-            // this wave's pieces: g = base + r with g = wave (mod P)
-            for (uint32_t r = (wave + P - base_mod) % P; r < total; r += P) {
+            // this wave's pieces: g = base + r with g = pw (mod P)
+            for (uint32_t r = (pw + P - base_mod) % P; r < total; r += P) {
                 const uint64_t owners = __ballot(e < q && excl <= r);
                 const int j = 63 - __builtin_clzll(owners);
                 const uint64_t c = r - (uint32_t)__builtin_amdgcn_readlane(excl, j);   // piece within entry j
-                const uint64_t di = (uint32_t)__builtin_amdgcn_readlane(v, j) - 1u;
+                const uint64_t di = (uint32_t)__builtin_amdgcn_readlane((uint32_t)v, j) - 1u;
                 const uint64_t bj = readfirstlane_u64(desc[di].bytes);
                 const uint64_t off = c * kBcChunk;
                 wave_copy(readfirstlane_u64(desc[di].src) + off, readfirstlane_u64(desc[di].dst) + off,
@@ -630,81 +663,16 @@ __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_c
         }
     }
 
-    // ---- 4. Completion, for the first `counted` workgroups only: they hold
-    // every wave that takes pieces and every scanner, so no other workgroup
-    // reads or writes the scratch, and the others leave here.  Counted
-    // workgroups count in per-XCD counters (`counted` is a multiple of 8, so
-    // each XCD group has counted / 8 members), the last of each group in one
-    // counter for the 8 groups: thousands of workgroups never serialise on
-    // one address.  Bits 0-15 count finished members, the
-    // bits above count members with a wave that did not take its pieces; the
-    // read-modify-write chain on one word carries that to the last workgroup
-    // out without any ordering between words.  The last workgroup then
-    // acquires the finished scan word (all slots visible), redoes the whole
-    // queue if any wave gave up (the same bytes written again), and clears
-    // the scratch for the next launch. ----
-    if (blockIdx.x >= counted)
-        return;
-    __shared__ uint32_t gave_up[kBcBlock / 64];
-    __shared__ uint32_t last_block;   // 0, 1 = last, 3 = last and redo the queue
-    if (lane == 0)
-        gave_up[wave_in_block] = takes_pieces && !sealed ? 1u : 0u;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t mine = 0;
-#pragma unroll
-        for (int k = 0; k < kBcBlock / 64; k++)
-            mine |= gave_up[k];
-        uint32_t last = 0;
-        const uint32_t x = blockIdx.x & 7;
-        const uint32_t old = atomic_add_agent(&scr->done_xcd[x].count, 1u | (mine << 16));
-        if ((old & 0xffffu) == counted / 8 - 1) {
-            atomic_store_agent(&scr->done_xcd[x].count, 0u);
-            const uint32_t group = ((old >> 16) | mine) != 0 ? 1u : 0u;
-            const uint32_t old_all = atomic_add_agent(&scr->done_all.count, 1u | (group << 16));
-            if ((old_all & 0xffffu) == 7)
-                last = ((old_all >> 16) | group) != 0 ? 3u : 1u;
-        }
-        last_block = last;
-    }
-    __syncthreads();
-    if (last_block) {
-        // Every scanner counted itself in the scan word before its workgroup
-        // was counted above, so the word is final; the waits below only cover
-        // the visibility of stores that have already been made, and are
-        // bounded all the same (about 10 ms).
-        const uint64_t deadline = (uint64_t)wall_clock64() + 8 * wait_ticks + 1000000u;
-        uint64_t sw = 0;
-        for (;;) {
-            sw = readfirstlane_u64(__hip_atomic_load(&scr->scan.word, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT));
-            if ((uint32_t)(sw >> 32) >= scanners || (uint64_t)wall_clock64() > deadline)
-                break;
-            __builtin_amdgcn_s_sleep(4);
-        }
-        const uint32_t qn = (uint32_t)sw < kBcQueueCap ? (uint32_t)sw : kBcQueueCap;
-        if (last_block == 3u) {
-            for (uint32_t e = wave_in_block; e < qn; e += kBcBlock / 64) {
-                // slot e was claimed, so its scanner has written it
-                uint32_t v;
-                for (;;) {
-                    v = __builtin_amdgcn_readfirstlane(atomic_load_agent(&scr->slot[e]));
-                    if (v != 0 || (uint64_t)wall_clock64() > deadline)
-                        break;
-                    __builtin_amdgcn_s_sleep(1);
-                }
-                if (slot_valid(v, n))
-                    wave_copy_any(readfirstlane_u64(desc[v - 1].src), readfirstlane_u64(desc[v - 1].dst),
-                                  readfirstlane_u64(desc[v - 1].bytes), lane);
-            }
-        }
-        __syncthreads();   // every wave has read its slots before any is cleared
-        for (uint32_t e = threadIdx.x; e < qn; e += kBcBlock)
-            atomic_store_agent(&scr->slot[e], 0u);
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            atomic_store_agent(&scr->scan.word, 0ull);
-            atomic_store_agent(&scr->done_all.count, 0u);
-        }
+    // ---- 4. A wave that gave up waiting, or met a slot it could not see,
+    // may have left pieces undone.  The first such wave of this launch (the
+    // epoch exchange elects it) copies every long copy of the batch whole,
+    // straight from the descriptor array; the others leave theirs to it. ----
+    if (!sealed) {
+        uint64_t prev = 0;
+        if (lane == 0)
+            prev = __hip_atomic_exchange(&scr->redo.word, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (readfirstlane_u64(prev) != epoch)
+            copy_all_long(desc, n, lane);
     }
 }
 
@@ -715,7 +683,7 @@ int batched_grid(uint32_t ncopies, int cu_count) {
         g = cus * kBcBlocksPerCu;
     if (g > cus * kBcMaxGridPerCu)
         g = cus * kBcMaxGridPerCu;
-    // a multiple of 8 (the completion counters are per XCD)
+    // a multiple of 8 (workgroups are dealt to the 8 XCDs in turn)
     return (int)((g + 7) & ~(uint64_t)7);
 }
 
@@ -728,23 +696,13 @@ uint32_t batched_scanners(uint32_t ncopies, int grid) {
     return s;
 }
 
-uint32_t batched_counted(uint32_t piece_waves, uint32_t scanners, int grid) {
-    uint32_t c = (piece_waves + kBcBlock / 64 - 1) / (kBcBlock / 64);   // workgroups holding piece waves
-    if (c < scanners)
-        c = scanners;
-    c = (c + 7) & ~7u;
-    return c < (uint32_t)grid ? c : (uint32_t)grid;   // grid is a multiple of 8
-}
-
-hipError_t launch_batched_copy(const tb_copy_desc *desc, uint32_t n, BcScratch *scratch, int cu_count,
-                               uint64_t wait_ticks, bool no_pieces, hipStream_t s) {
+hipError_t launch_batched_copy(const tb_copy_desc *desc, uint32_t n, BcScratch *scratch, uint64_t epoch,
+                               int cu_count, uint64_t wait_ticks, bool no_pieces, hipStream_t s) {
     const int grid = batched_grid(n, cu_count);
-    // pieces of long copies go to the waves resident from the start: CUs x 8
-    // waves per SIMD x 4 SIMDs at most
+    // pieces of long copies go to as many waves as fit on the chip at once
     const uint32_t resident = (uint32_t)(cu_count > 0 ? cu_count : 1) * kBcResidentWavesPerCu;
-    const uint32_t scanners = batched_scanners(n, grid);
-    hipLaunchKernelGGL(bc_kernel, dim3(grid), dim3(kBcBlock), 0, s, desc, n, scratch, scanners, wait_ticks, resident,
-                       batched_counted(resident, scanners, grid), no_pieces ? 1u : 0u);
+    hipLaunchKernelGGL(bc_kernel, dim3(grid), dim3(kBcBlock), 0, s, desc, n, scratch, epoch,
+                       batched_scanners(n, grid), wait_ticks, resident, no_pieces ? 1u : 0u);
     return hipGetLastError();
 }
 

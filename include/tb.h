@@ -184,7 +184,8 @@ int tb_reduce_copy_ex(float *dst, const float *const *srcs, int32_t nsrc,
  * the descriptors are in device memory).
  * The kernel uses a small library-owned scratch area per (device, stream),
  * allocated on the first call for that pair; calls on one stream are ordered,
- * calls on different streams use different scratch.
+ * calls on different streams use different scratch (each launch relies on the
+ * previous launch on its scratch having finished).
  * Errors: TB_ERR_INVALID for a NULL or misaligned desc_dev with ncopies > 0;
  * TB_ERR_NOMEM if the scratch cannot be allocated; TB_ERR_HIP.
  */
@@ -194,13 +195,13 @@ int tb_batched_copy(const tb_copy_desc *desc_dev, uint32_t ncopies, void *stream
  * Test hook for the batched copy's recovery path (process-wide; affects
  * launches made after the call).  Long copies go through a queue whose pieces
  * the waves share once every scanning workgroup has published; the wait for
- * that is bounded, and a wave that gives up leaves the queue to the last
- * workgroup to finish, which copies all of it again.  Modes:
+ * that is bounded, and a wave that gives up leaves its pieces to the first
+ * wave of the launch that gave up, which copies every long copy of the batch
+ * whole.  Modes:
  *   TB_BC_NORMAL     waves wait up to 200 us of device time (the default);
  *   TB_BC_NO_WAIT    waves do not wait: any that find the queue unfinished
  *                    give up;
- *   TB_BC_LAST_ONLY  every wave gives up: the last workgroup copies the
- *                    whole queue.
+ *   TB_BC_LAST_ONLY  every wave gives up: one wave copies every long copy.
  * The bytes written are identical in every mode; only the speed differs.
  * Errors: TB_ERR_INVALID for an unknown mode.
  */

@@ -241,3 +241,22 @@ def test_torch_conveniences_reject_out_of_range_counts():
     reduce_copy(dst, [src], nfloats=100)
     batched_copy(desc, ncopies=0)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("mode", ["TB_BC_NORMAL", "TB_BC_NO_WAIT"])
+def test_consecutive_launches_alternate_batches(mode):
+    """Launches on one stream reuse one scratch: the scan words alternate by
+    launch and queue slots carry the launch's number, so batches with and
+    without long copies may follow each other in any order."""
+    torch = require_gpu()
+    import copy_reduce_amd as tb
+    batches = [_long_and_short_batch(31), wl.batch_random(32, 900, max_bytes=3000, pool_bytes=8 << 20),
+               _long_and_short_batch(33)]
+    order = [0, 1, 2, 0, 2, 1, 1, 0]
+    tb.tb_batched_set_mode(getattr(tb, mode))
+    try:
+        for step, k in enumerate(order):
+            note(f"batched alternating mode={mode} step={step} batch={k}")
+            assert _run_batch(torch, batches[k], src_shift=step % 5, dst_shift=(3 * step) % 7) == -1
+    finally:
+        tb.tb_batched_set_mode(tb.TB_BC_NORMAL)
