@@ -52,4 +52,7 @@ def test_one_call_per_descriptor(kind):
     exp = np.full(b.pool_bytes, wl.POOL_FILL, dtype=np.uint8)
     oracle.ref_batch(exp, b.payload, b.desc)
     assert oracle.first_mismatch(pool.cpu().numpy(), exp) == -1
-    assert bench.batch_sample_check(torch, pool, b)
+    assert bench.batch_sample_check(torch, pool, b, src)
+    k = int(np.flatnonzero(b.desc[:, 2] > 0)[0])
+    pool[int(b.desc[k, 1])] ^= 0xFF        # one flipped byte must be caught
+    assert not bench.batch_sample_check(torch, pool, b, src)
