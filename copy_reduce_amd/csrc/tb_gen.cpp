@@ -101,32 +101,35 @@ void fill_compress(float *out, uint64_t n, int32_t b, const uint32_t pct[5], uin
 
 extern "C" int tb_prep_reference(float *host_out, uint64_t nfloats, int32_t buffer_idx,
                                  const tb_fill_cfg *cfg) {
+    // the configuration is checked first, whatever the size
     if (buffer_idx < 0)
         return TB_ERR_INVALID;
-    if (nfloats == 0)
-        return TB_OK;
-    if (host_out == nullptr || nfloats > UINT64_MAX / 4)
-        return TB_ERR_INVALID;
     const int32_t kind = cfg ? cfg->kind : TB_FILL_DEFAULT;
-    switch (kind) {
-    case TB_FILL_DEFAULT:
-        fill_default(host_out, nfloats, buffer_idx);
-        return TB_OK;
-    case TB_FILL_PATTERN:
-        if (cfg->pattern == nullptr || cfg->pattern_len == 0)
-            return TB_ERR_INVALID;
-        fill_pattern(host_out, nfloats, cfg->pattern, cfg->pattern_len);
-        return TB_OK;
-    case TB_FILL_COMPRESS: {
+    if (kind == TB_FILL_PATTERN && (cfg->pattern == nullptr || cfg->pattern_len == 0))
+        return TB_ERR_INVALID;
+    if (kind == TB_FILL_COMPRESS) {
         uint64_t sum = 0;
         for (int c = 0; c < 5; c++)
             sum += cfg->compress_pct[c];
         if (sum != 100)
             return TB_ERR_INVALID;
-        fill_compress(host_out, nfloats, buffer_idx, cfg->compress_pct, cfg->seed);
-        return TB_OK;
     }
-    default:
+    if (kind != TB_FILL_DEFAULT && kind != TB_FILL_PATTERN && kind != TB_FILL_COMPRESS)
         return TB_ERR_INVALID;
+    if (nfloats == 0)
+        return TB_OK;
+    if (host_out == nullptr || nfloats > UINT64_MAX / 4)
+        return TB_ERR_INVALID;
+    switch (kind) {
+    case TB_FILL_DEFAULT:
+        fill_default(host_out, nfloats, buffer_idx);
+        break;
+    case TB_FILL_PATTERN:
+        fill_pattern(host_out, nfloats, cfg->pattern, cfg->pattern_len);
+        break;
+    default:
+        fill_compress(host_out, nfloats, buffer_idx, cfg->compress_pct, cfg->seed);
+        break;
     }
+    return TB_OK;
 }
