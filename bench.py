@@ -85,6 +85,7 @@ def device_record(torch, tb):
     import glob
     props = torch.cuda.get_device_properties(0)
     rec = {"name": props.name or torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", ""),
+           "hip_runtime": getattr(torch.version, "hip", None),
            "cu_count": tb.tb_launch_info()["cu_count"],
            "hbm_bytes": int(props.total_memory)}
     for key, fname in (("compute_partition", "current_compute_partition"),
@@ -117,6 +118,7 @@ def setup_batch(torch, tb, batch, rotate_bytes):
     and one descriptor array per replica; pool pre-filled with 0xA5."""
     import workloads as wl
     from copy_reduce_amd.torch_api import make_desc
+    batch.check()
     kb = tb.tb_num_slices(batch.total_bytes, rotate_bytes)
     stride = tb.tb_slice_stride(batch.src_bytes)
     src = torch.empty(max(1, kb * stride), dtype=torch.uint8, device="cuda")

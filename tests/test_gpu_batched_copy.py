@@ -18,6 +18,7 @@ def _run_batch(torch, batch: wl.Batch, src_shift: int = 0, dst_shift: int = 0, s
     src_shift / dst_shift move the base addresses off 256-byte alignment."""
     import copy_reduce_amd as tb
     from copy_reduce_amd.torch_api import make_desc
+    batch.check()
     src = torch.empty(batch.src_bytes + 64, dtype=torch.uint8, device="cuda")
     if batch.src_bytes:
         src[src_shift:src_shift + batch.src_bytes].copy_(torch.from_numpy(batch.payload[:batch.src_bytes]))

@@ -291,6 +291,22 @@ def test_c4_c5_shapes():
     assert int(d[-1] + s[-1]) <= c5.pool_bytes
 
 
+def test_batch_preconditions_hold_and_are_checked():
+    """Every workload satisfies the batched copy's preconditions (disjoint,
+    in-range destinations), and the check rejects a batch that does not."""
+    for b in (wl.batch_c4(with_payload=False), wl.batch_c5(with_payload=False),
+              wl.batch_random(3, 500, max_bytes=5000, pool_bytes=8 << 20)):
+        assert b.check() is b
+    bad = wl.batch_random(4, 10, max_bytes=100, pool_bytes=1 << 16, min_bytes=8)
+    bad.desc[1, 1] = bad.desc[0, 1] + 1                      # overlaps copy 0
+    with pytest.raises(ValueError):
+        bad.check()
+    far = wl.batch_random(5, 10, max_bytes=100, pool_bytes=1 << 16, min_bytes=8)
+    far.desc[0, 1] = far.pool_bytes                          # past the pool
+    with pytest.raises(ValueError):
+        far.check()
+
+
 # --------------------------------------------------------------------------
 # Comparator ("How validation (ValidateAllTransfers) works")
 # --------------------------------------------------------------------------

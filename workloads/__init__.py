@@ -102,6 +102,26 @@ class Batch:
         """Read plus write of every payload byte: 2 x sum(bytes)."""
         return 2 * self.total_bytes
 
+    def check(self) -> "Batch":
+        """Preconditions the batched copy assumes and cannot check on the
+        device: every source range inside the source image, every destination
+        range inside the pool, destination ranges pairwise disjoint.  Raises
+        ValueError; returns self."""
+        d = self.desc.astype(np.uint64)
+        if d.ndim != 2 or d.shape[1] != 3:
+            raise ValueError("descriptors must be an (n, 3) array")
+        s, t, b = (d[:, k].astype(object) for k in range(3))   # exact integers
+        if any(x + y > self.src_bytes for x, y in zip(s, b)):
+            raise ValueError("a source range lies outside the source image")
+        if any(x + y > self.pool_bytes for x, y in zip(t, b)):
+            raise ValueError("a destination range lies outside the pool")
+        live = np.flatnonzero(d[:, 2] > 0)
+        order = live[np.argsort(d[live, 1], kind="stable")]
+        ends = d[order, 1] + d[order, 2]
+        if np.any(ends[:-1] > d[order[1:], 1]):
+            raise ValueError("destination ranges overlap")
+        return self
+
 
 def log_uniform_sizes(rng: np.random.Generator, n: int, lo: int, hi: int,
                       granule: int = 64) -> np.ndarray:
