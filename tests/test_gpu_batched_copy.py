@@ -261,3 +261,22 @@ def test_consecutive_launches_alternate_batches(mode):
             assert _run_batch(torch, batches[k], src_shift=step % 5, dst_shift=(3 * step) % 7) == -1
     finally:
         tb.tb_batched_set_mode(tb.TB_BC_NORMAL)
+
+
+def test_shutdown_frees_scratch_and_later_calls_start_afresh():
+    """tb_shutdown waits for the device and frees the library's scratch and
+    gate memory; later calls allocate them again (launch numbering restarts
+    on the new scratch), and a second shutdown is harmless."""
+    torch = require_gpu()
+    import copy_reduce_amd as tb
+    batch = _long_and_short_batch(41)
+    note("batched shutdown / relaunch")
+    assert _run_batch(torch, batch, launches=3) == -1
+    tb.tb_shutdown()
+    tb.tb_shutdown()
+    assert _run_batch(torch, batch, launches=2) == -1
+    stream = torch.cuda.current_stream().cuda_stream
+    tb.tb_spin_gate_arm(1000, stream)
+    tb.tb_spin_gate_release()
+    torch.cuda.synchronize()
+    assert tb.tb_spin_gate_status() == tb.TB_OK
