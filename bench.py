@@ -374,6 +374,10 @@ def suite(args, torch, tb, wl):
         for rot in (True, False):
             sw = wl.sweep_workload(nbytes, rot)
             entries.append((sw.name, lambda sw=sw: reduce_line(sw, reps=3)))
+    # how the reduce-copy scales with the number of sources (64 MiB each, R = 256 MiB)
+    for nsrc in (1, 2, 3, 4, 6, 8, 12, 16):
+        nw = wl.ReduceWorkload(f"nsweep_N{nsrc}_64MiB", nsrc, 16 << 20, wl.DEFAULT_ROTATE_BYTES)
+        entries.append((nw.name, lambda nw=nw: reduce_line(nw)))
     names = [n for n, _ in entries]
     only = [n for n in (args.only or "").split(",") if n]
     unknown = [n for n in only if n not in names]

@@ -17,7 +17,7 @@ TB_ERR_NOMEM = -3
 TB_ERR_TIMEOUT = -4
 TB_MAX_SRCS = 16
 TB_FILL_DEFAULT, TB_FILL_PATTERN, TB_FILL_COMPRESS = 0, 1, 2
-TB_BC_NORMAL, TB_BC_NO_WAIT, TB_BC_LAST_ONLY = 0, 1, 2
+TB_BC_NORMAL, TB_BC_NO_WAIT, TB_BC_NO_PIECES = 0, 1, 2
 
 # Every symbol include/tb.h declares.
 EXPORTS = (

@@ -266,7 +266,7 @@ int tb_reduce_copy(float *dst, const float *const *srcs, int32_t nsrc, uint64_t 
 static std::atomic<int> g_batched_mode{TB_BC_NORMAL};
 
 int tb_batched_set_mode(int32_t mode) {
-    if (mode != TB_BC_NORMAL && mode != TB_BC_NO_WAIT && mode != TB_BC_LAST_ONLY)
+    if (mode != TB_BC_NORMAL && mode != TB_BC_NO_WAIT && mode != TB_BC_NO_PIECES)
         return TB_ERR_INVALID;
     g_batched_mode.store(mode, std::memory_order_relaxed);
     return TB_OK;
@@ -291,7 +291,7 @@ int tb_batched_copy(const tb_copy_desc *desc_dev, uint32_t ncopies, void *stream
     const uint64_t wait_ticks =
         mode == TB_BC_NORMAL ? (uint64_t)tbk::kBcSealWaitUs * info.wall_clock_khz / 1000u : 0u;
     hipError_t e = tbk::launch_batched_copy(desc_dev, ncopies, scratch, epoch, info.cu_count, wait_ticks,
-                                            mode == TB_BC_LAST_ONLY, s);
+                                            mode == TB_BC_NO_PIECES, s);
     if (e != hipSuccess)
         return hip_fail(e, "batched-copy launch");
     return TB_OK;

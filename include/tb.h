@@ -201,11 +201,11 @@ int tb_batched_copy(const tb_copy_desc *desc_dev, uint32_t ncopies, void *stream
  *   TB_BC_NORMAL     waves wait up to 200 us of device time (the default);
  *   TB_BC_NO_WAIT    waves do not wait: any that find the queue unfinished
  *                    give up;
- *   TB_BC_LAST_ONLY  every wave gives up: one wave copies every long copy.
+ *   TB_BC_NO_PIECES  no wave takes pieces: one wave copies every long copy.
  * The bytes written are identical in every mode; only the speed differs.
  * Errors: TB_ERR_INVALID for an unknown mode.
  */
-enum { TB_BC_NORMAL = 0, TB_BC_NO_WAIT = 1, TB_BC_LAST_ONLY = 2 };
+enum { TB_BC_NORMAL = 0, TB_BC_NO_WAIT = 1, TB_BC_NO_PIECES = 2 };
 int tb_batched_set_mode(int32_t mode);
 
 /*

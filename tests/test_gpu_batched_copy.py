@@ -163,7 +163,7 @@ def test_same_batch_moved_by_three_bytes_between_calls():
     assert _run_batch(torch, batch, launches=1) == -1
 
 
-@pytest.mark.parametrize("mode", ["TB_BC_NO_WAIT", "TB_BC_LAST_ONLY"])
+@pytest.mark.parametrize("mode", ["TB_BC_NO_WAIT", "TB_BC_NO_PIECES"])
 @pytest.mark.parametrize("case", ["long_short", "c5_256MiB_pool", "overflow"])
 def test_recovery_path_gives_identical_bytes(mode, case):
     """Waves that do not wait for the long-copy queue leave it to the last

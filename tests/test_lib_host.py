@@ -174,7 +174,7 @@ def test_batched_copy_argument_checks():
 def test_batched_mode_hook_checks():
     for bad in (-1, 3, 1 << 20):
         assert _st("tb_batched_set_mode", bad) == tb.TB_ERR_INVALID
-    for good in (tb.TB_BC_NO_WAIT, tb.TB_BC_LAST_ONLY, tb.TB_BC_NORMAL):   # ends in the default
+    for good in (tb.TB_BC_NO_WAIT, tb.TB_BC_NO_PIECES, tb.TB_BC_NORMAL):   # ends in the default
         assert _st("tb_batched_set_mode", good) == tb.TB_OK
 
 
