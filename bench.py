@@ -689,6 +689,136 @@ def interference(args, torch, tb, wl):
 
 
 # ---------------------------------------------------------------------------
+# --ring: the descriptor-slot ring's host cost and end-to-end rate
+# ---------------------------------------------------------------------------
+
+def ring_study(args, torch, tb, wl):
+    """The descriptor-slot ring (Mooncake RFC #5041, Design of #5040,
+    "Descriptor slots" and "Host trims"): host nanoseconds per request and per
+    copy for submit and poll, and the end-to-end rate of the 47,520-copy and the
+    mixed KV batches cut into requests, through staged and direct rings of 32
+    slots x 8,192 descriptors; beside them, one tb_batched_copy of the whole
+    batch from device memory.  The C calls are made through ctypes directly;
+    the ctypes floor (a trivial library call) is reported with them."""
+    import ctypes
+    import numpy as np
+
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    lib = tb.lib
+    ns = time.perf_counter_ns
+    print(json.dumps({"ring_device": device_record(torch, tb)}), flush=True)
+
+    def floor_ns(reps=20000):
+        t0 = ns()
+        for _ in range(reps):
+            lib.tb_batched_set_mode(0)
+        return (ns() - t0) / reps
+
+    def one_pass(ring, host, cuts):
+        """Submit every request of one batch, then poll the last ticket until
+        done.  Returns host ns of the submits made while every slot was free,
+        of all submits, per pending poll, the number of polls, and the wall ns."""
+        t = ctypes.c_uint64()
+        done = ctypes.c_int32()
+        base = host.ctypes.data
+        free_ns = all_ns = 0
+        t0 = ns()
+        for j, (a, m) in enumerate(cuts):
+            s0 = ns()
+            rc = lib.tb_ring_submit(ring, base + 24 * a, m, ctypes.byref(t))
+            dt = ns() - s0
+            if rc != 0:
+                raise tb.TBError("tb_ring_submit", rc)
+            all_ns += dt
+            if j < 32:
+                free_ns += dt
+        polls, p_ns = 0, 0
+        while True:
+            s0 = ns()
+            rc = lib.tb_ring_poll(ring, t.value, ctypes.byref(done))
+            p_ns += ns() - s0
+            polls += 1
+            if rc != 0:
+                raise tb.TBError("tb_ring_poll", rc)
+            if done.value:
+                break
+        return free_ns, all_ns, p_ns / polls, polls, ns() - t0
+
+    floor = floor_ns()
+    for batch in (wl.batch_c4(), wl.batch_c5()):
+        b = setup_batch(torch, tb, batch, wl.DEFAULT_ROTATE_BYTES)
+        pool_base = int(b["pool"].data_ptr())
+        hosts = []
+        for r in range(b["kb"]):
+            d = batch.desc.astype(np.uint64).copy()
+            d[:, 0] += np.uint64(b["base"] + r * b["stride"])
+            d[:, 1] += np.uint64(pool_base)
+            hosts.append(np.ascontiguousarray(d))
+        n = batch.ncopies
+        # one launch of the whole batch from device memory, host wall clock to the end
+        walls = []
+        for i in range(-args.warmup, args.steps):
+            torch.cuda.synchronize()
+            t0 = ns()
+            tb.tb_batched_copy(int(batch_desc_for(tb, b, i).data_ptr()), n, sh)
+            stream.synchronize()
+            if i >= 0:
+                walls.append(ns() - t0)
+        ref_us = statistics.median(walls) / 1e3
+        print(json.dumps({"ring": {"batch": batch.name, "ncopies": n, "path": "tb_batched_copy, device descriptors",
+                                   "wall_us": round(ref_us, 2),
+                                   "gbps": round(batch.algorithmic_bytes / (ref_us * 1e-6) / 1e9, 1)}}), flush=True)
+        for kind in (tb.TB_RING_STAGED, tb.TB_RING_DIRECT):
+            ring = tb.tb_ring_create(32, 8192, kind, sh)
+            try:
+                for req in (16, 256, 4096, 8192):
+                    cuts = [(a, min(req, n - a)) for a in range(0, n, req)]
+                    rows = []
+                    for i in range(-args.warmup, args.steps):
+                        r = one_pass(ring, hosts[replica_of(tb, b, i)], cuts)
+                        if i >= 0:
+                            rows.append(r)
+                    free_n = min(32, len(cuts))
+                    free_copies = sum(m for _, m in cuts[:free_n])
+                    wall_us = statistics.median([r[4] for r in rows]) / 1e3
+                    sub_free = statistics.median([r[0] for r in rows])
+                    rec = {"batch": batch.name, "ncopies": n,
+                           "path": "ring " + ("direct" if kind == tb.TB_RING_DIRECT else "staged"),
+                           "slots": "32 x 8192", "copies_per_request": req, "requests": len(cuts),
+                           "submit_ns_per_request_slots_free": round(sub_free / free_n),
+                           "submit_ns_per_copy_slots_free": round(sub_free / free_copies, 1),
+                           "submit_ns_per_request_all": round(statistics.median([r[1] for r in rows]) / len(cuts)),
+                           "poll_ns_pending": round(statistics.median([r[2] for r in rows])),
+                           "polls_per_pass": int(statistics.median([r[3] for r in rows])),
+                           "ctypes_floor_ns": round(floor),
+                           "wall_us": round(wall_us, 2),
+                           "gbps": round(batch.algorithmic_bytes / (wall_us * 1e-6) / 1e9, 1),
+                           "copies_per_s": round(n / (wall_us * 1e-6), 0)}
+                    print(json.dumps({"ring": rec}), flush=True)
+                # a poll answered from the ring's record of finished tickets
+                t = ctypes.c_uint64()
+                done = ctypes.c_int32()
+                lib.tb_ring_submit(ring, None, 0, ctypes.byref(t))
+                t0 = ns()
+                for _ in range(20000):
+                    lib.tb_ring_poll(ring, t.value, ctypes.byref(done))
+                cached = (ns() - t0) / 20000
+            finally:
+                tb.tb_ring_destroy(ring)
+            print(json.dumps({"ring_poll_cached": {"path": "ring " + ("direct" if kind == tb.TB_RING_DIRECT
+                                                                       else "staged"),
+                                                   "poll_ns": round(cached), "ctypes_floor_ns": round(floor)}}),
+                  flush=True)
+        ok = batch_sample_check(torch, b["pool"], batch, b["src"])
+        print(json.dumps({"ring_validated_sample": {"batch": batch.name, "ok": ok}}), flush=True)
+        if not ok:
+            raise RuntimeError(f"ring copies of {batch.name} differ from their sources")
+        del b
+        torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
 # --roofs: what this chip's HBM sustains for reads, writes and their mix
 # ---------------------------------------------------------------------------
 
@@ -758,6 +888,8 @@ def main():
                          "descriptor) on the same inputs, then exit")
     ap.add_argument("--interference", action="store_true",
                     help="only time C4 (batched, and one call per descriptor) alone and beside a bf16 GEMM, then exit")
+    ap.add_argument("--ring", action="store_true",
+                    help="only time the descriptor-slot ring (host submit/poll cost, end-to-end rate), then exit")
     ap.add_argument("--roofs", action="store_true",
                     help="only time write-only, read-mostly and copy streams larger than the memory-side cache, then exit")
     ap.add_argument("--cache-study", action="store_true",
@@ -800,6 +932,9 @@ def main():
         return
     if args.interference:
         interference(args, torch, tb, wl)
+        return
+    if args.ring:
+        ring_study(args, torch, tb, wl)
         return
     if args.suite or args.only:
         suite(args, torch, tb, wl)

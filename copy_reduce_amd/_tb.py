@@ -18,6 +18,7 @@ TB_ERR_TIMEOUT = -4
 TB_MAX_SRCS = 16
 TB_FILL_DEFAULT, TB_FILL_PATTERN, TB_FILL_COMPRESS = 0, 1, 2
 TB_BC_NORMAL, TB_BC_NO_WAIT, TB_BC_NO_PIECES = 0, 1, 2
+TB_RING_STAGED, TB_RING_DIRECT = 0, 1
 
 # Every symbol include/tb.h declares.
 EXPORTS = (
@@ -25,6 +26,7 @@ EXPORTS = (
     "tb_status_string", "tb_last_hip_error", "tb_prep_sources", "tb_reduce_copy",
     "tb_reduce_copy_ex", "tb_batched_copy", "tb_batched_set_mode", "tb_spin_gate_arm", "tb_spin_gate_release",
     "tb_spin_gate_status", "tb_launch_info", "tb_shutdown",
+    "tb_ring_create", "tb_ring_submit", "tb_ring_poll", "tb_ring_wait", "tb_ring_destroy",
 )
 
 # torch ships its own HIP runtime under the same soname (libamdhip64.so.7) as
@@ -71,6 +73,11 @@ _SIGS = {
     "tb_launch_info": (ctypes.c_int, [_u64, _i32, _u32, ctypes.POINTER(_i32), ctypes.POINTER(_i32),
                                       ctypes.POINTER(_i32)]),
     "tb_shutdown": (ctypes.c_int, []),
+    "tb_ring_create": (ctypes.c_int, [_u32, _u32, _u32, _vp, ctypes.POINTER(_vp)]),
+    "tb_ring_submit": (ctypes.c_int, [_vp, _vp, _u64, ctypes.POINTER(_u64)]),
+    "tb_ring_poll": (ctypes.c_int, [_vp, _u64, ctypes.POINTER(_i32)]),
+    "tb_ring_wait": (ctypes.c_int, [_vp, _u64]),
+    "tb_ring_destroy": (ctypes.c_int, [_vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(lib, _name)
@@ -198,3 +205,33 @@ def tb_spin_gate_status() -> int:
 
 def tb_shutdown() -> None:
     _check("tb_shutdown", lib.tb_shutdown())
+
+
+# ---------------------------------------------------------------- descriptor-slot ring
+
+def tb_ring_create(nslots: int, slot_descs: int, flags: int, stream: int) -> int:
+    """A new ring on the current device and `stream`; returns its handle."""
+    out = _vp()
+    _check("tb_ring_create", lib.tb_ring_create(nslots, slot_descs, flags, stream, ctypes.byref(out)))
+    return int(out.value)
+
+
+def tb_ring_submit(ring: int, host_desc_ptr: int, n: int) -> int:
+    """Submit n host descriptors at host_desc_ptr; returns the ticket."""
+    t = _u64()
+    _check("tb_ring_submit", lib.tb_ring_submit(ring, host_desc_ptr, n, ctypes.byref(t)))
+    return t.value
+
+
+def tb_ring_poll(ring: int, ticket: int) -> bool:
+    done = _i32()
+    _check("tb_ring_poll", lib.tb_ring_poll(ring, ticket, ctypes.byref(done)))
+    return bool(done.value)
+
+
+def tb_ring_wait(ring: int, ticket: int) -> None:
+    _check("tb_ring_wait", lib.tb_ring_wait(ring, ticket))
+
+
+def tb_ring_destroy(ring: int) -> None:
+    _check("tb_ring_destroy", lib.tb_ring_destroy(ring))

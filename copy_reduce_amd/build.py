@@ -17,7 +17,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtb.so")
 ARCH = "gfx950"
 
-SOURCES = ["tb_host.cpp", "tb_gen.cpp", "tb_kernels.hip"]
+SOURCES = ["tb_host.cpp", "tb_gen.cpp", "tb_ring.cpp", "tb_kernels.hip"]
 
 COMMON = [
     "-std=c++17", "-O3", "-fPIC", "-Wall", "-Wextra", "-Werror",

@@ -14,13 +14,25 @@
 #include "tb_internal.h"
 
 namespace {
-
 thread_local std::string g_last_hip_error;
+// How the batched copy shares its long copies (TB_BC_*): process-wide.
+std::atomic<int> g_batched_mode{TB_BC_NORMAL};
+}  // namespace
+
+namespace tbh {
 
 int hip_fail(hipError_t e, const char *what) {
     g_last_hip_error = std::string(what) + ": " + hipGetErrorName(e) + " (" + hipGetErrorString(e) + ")";
     return TB_ERR_HIP;
 }
+
+int batched_mode() { return g_batched_mode.load(std::memory_order_relaxed); }
+
+}  // namespace tbh
+
+namespace {
+
+using tbh::hip_fail;
 
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
@@ -261,9 +273,6 @@ int tb_reduce_copy_ex(float *dst, const float *const *srcs, int32_t nsrc, uint64
 int tb_reduce_copy(float *dst, const float *const *srcs, int32_t nsrc, uint64_t nfloats, void *stream) {
     return tb_reduce_copy_ex(dst, srcs, nsrc, nfloats, 0u, stream);
 }
-
-// How the batched copy shares its long copies (TB_BC_*): process-wide.
-static std::atomic<int> g_batched_mode{TB_BC_NORMAL};
 
 int tb_batched_set_mode(int32_t mode) {
     if (mode != TB_BC_NORMAL && mode != TB_BC_NO_WAIT && mode != TB_BC_NO_PIECES)

@@ -67,11 +67,6 @@ constexpr uint32_t kBcScanPerBlock = 1024;
 // Longest wait for the queue to be sealed, in microseconds of device time.
 constexpr uint32_t kBcSealWaitUs = 200;
 
-struct alignas(256) BcCounter {
-    uint32_t count;
-    uint32_t pad[63];
-};
-
 struct alignas(256) BcWord {
     uint64_t word;
     uint64_t pad[31];
@@ -105,6 +100,14 @@ uint32_t batched_scanners(uint32_t ncopies, int grid);
 hipError_t launch_batched_copy(const tb_copy_desc *desc, uint32_t n, BcScratch *scratch, uint64_t epoch,
                                int cu_count, uint64_t wait_ticks, bool no_pieces, hipStream_t stream);
 
+// As launch_batched_copy, for a batch the caller has checked holds no copy
+// longer than kBcSplitAbove: the queue is skipped (no scanner workgroups, no
+// piece waves, no wait) and the grid has one descriptor per wave with no
+// floor.  The launch still clears the scan word of the next epoch, so any
+// launch may follow it on the same scratch.
+hipError_t launch_batched_copy_short(const tb_copy_desc *desc, uint32_t n, BcScratch *scratch, uint64_t epoch,
+                                     int cu_count, hipStream_t stream);
+
 // ---- spin gate ---------------------------------------------------------------
 
 // One thread waits until *flag != 0, or until timeout_ticks of the device
@@ -113,3 +116,15 @@ hipError_t launch_spin_gate(const uint32_t *flag, uint32_t *timed_out, uint64_t 
                             hipStream_t stream);
 
 }  // namespace tbk
+
+// ---- host helpers shared by the host sources (tb_host.cpp defines them) -------
+
+namespace tbh {
+
+// Record `what` and e's text for tb_last_hip_error(); returns TB_ERR_HIP.
+int hip_fail(hipError_t e, const char *what);
+
+// The TB_BC_* mode last set by tb_batched_set_mode.
+int batched_mode();
+
+}  // namespace tbh

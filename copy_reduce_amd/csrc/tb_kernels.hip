@@ -706,6 +706,20 @@ hipError_t launch_batched_copy(const tb_copy_desc *desc, uint32_t n, BcScratch *
     return hipGetLastError();
 }
 
+hipError_t launch_batched_copy_short(const tb_copy_desc *desc, uint32_t n, BcScratch *scratch, uint64_t epoch,
+                                     int cu_count, hipStream_t s) {
+    // no scanners and no piece waves: every wave copies its own descriptors
+    // and is done; one descriptor per wave, no floor on the grid
+    const uint64_t cus = (uint64_t)(cu_count > 0 ? cu_count : 1);
+    uint64_t g = ((uint64_t)n + kBcDescPerWave * 4 - 1) / (kBcDescPerWave * 4);
+    if (g > cus * kBcMaxGridPerCu)
+        g = cus * kBcMaxGridPerCu;
+    const int grid = (int)((g + 7) & ~(uint64_t)7);
+    hipLaunchKernelGGL(bc_kernel, dim3(grid), dim3(kBcBlock), 0, s, desc, n, scratch, epoch, 0u, (uint64_t)0, 0u,
+                       0u);
+    return hipGetLastError();
+}
+
 // ============================================================================
 // Spin gate ("nvbandwidth deep dive" §3.3.1): hold the stream until the host
 // releases it, so queued launches and events then run back to back.  Bounded:

@@ -6,6 +6,7 @@ host memory and streams; every step of the path runs in libtb.
     reduce_copy      tb_reduce_copy on tensors / raw device addresses
     make_desc        (src_off, dst_off, bytes) offsets -> device tb_copy_desc array
     batched_copy     tb_batched_copy on a device descriptor tensor
+    DescRing         tb_ring_* (descriptor-slot ring) over host descriptor arrays
 """
 from typing import List, Optional, Sequence
 
@@ -105,3 +106,34 @@ def batched_copy(desc: torch.Tensor, ncopies: Optional[int] = None,
     if not 0 <= n <= desc.shape[0]:
         raise ValueError("ncopies must be between 0 and the number of descriptors in desc")
     _tb.tb_batched_copy(desc.data_ptr(), n, stream_handle(stream))
+
+
+class DescRing:
+    """Descriptor-slot ring on the current device: submit host (n, 3) uint64
+    descriptor arrays (absolute src, dst, bytes) and poll their tickets."""
+
+    def __init__(self, nslots: int = 32, slot_descs: int = 8192, direct: bool = False,
+                 stream: Optional[torch.cuda.Stream] = None):
+        self.handle = _tb.tb_ring_create(nslots, slot_descs, _tb.TB_RING_DIRECT if direct else _tb.TB_RING_STAGED,
+                                         stream_handle(stream))
+
+    def submit(self, desc: np.ndarray) -> int:
+        d = np.ascontiguousarray(desc, dtype=np.uint64).reshape(-1, 3)
+        return _tb.tb_ring_submit(self.handle, d.ctypes.data, d.shape[0])
+
+    def poll(self, ticket: int) -> bool:
+        return _tb.tb_ring_poll(self.handle, ticket)
+
+    def wait(self, ticket: int) -> None:
+        _tb.tb_ring_wait(self.handle, ticket)
+
+    def close(self) -> None:
+        if self.handle:
+            h, self.handle = self.handle, 0
+            _tb.tb_ring_destroy(h)
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()

@@ -7,7 +7,8 @@
  *     through rotated source slices so that repeated launches cannot be served
  *     from cache;
  *   - a batched copy that runs a whole (src, dst, bytes) descriptor array in
- *     one launch.
+ *     one launch, also submitted from host descriptor lists through a ring of
+ *     descriptor slots.
  *
  * Conventions for every entry point:
  *   - Calls return a tb_status and never throw; the library prints nothing.
@@ -17,7 +18,8 @@
  *     stream.  GPU work is only enqueued: no call below synchronises unless it
  *     says so, and the library never touches a stream it was not given.
  *   - The caller owns every buffer it passes.  The library owns only the
- *     batched-copy scratch and the spin-gate flag (freed by tb_shutdown).
+ *     batched-copy scratch and the spin-gate flag (freed by tb_shutdown) and
+ *     what a descriptor-slot ring holds (freed by tb_ring_destroy).
  *   - TB_ERR_HIP means a HIP runtime call failed; tb_last_hip_error() gives
  *     its text.  Faults inside a kernel surface at the caller's next
  *     synchronisation, as for any HIP kernel.
@@ -207,6 +209,63 @@ int tb_batched_copy(const tb_copy_desc *desc_dev, uint32_t ncopies, void *stream
  */
 enum { TB_BC_NORMAL = 0, TB_BC_NO_WAIT = 1, TB_BC_NO_PIECES = 2 };
 int tb_batched_set_mode(int32_t mode);
+
+/*
+ * Descriptor-slot ring (Mooncake RFC #5041, Design of #5040, "Descriptor
+ * slots" and "Host trims"): batched copies whose descriptors the caller holds
+ * in HOST memory, submitted without blocking and polled for completion.
+ *
+ * A ring is bound at creation to the current device and to `stream`, and
+ * owns: nslots slots of slot_descs descriptors each in pinned host memory;
+ * unless TB_RING_DIRECT, a device copy of every slot; one completion event
+ * per slot; and its own batched-copy scratch.  tb_ring_submit takes the
+ * caller's descriptors into the next slot, enqueues on the ring's stream
+ *   TB_RING_STAGED: a host-to-device copy of the slot, then the batched copy
+ *                   reading the device copy;
+ *   TB_RING_DIRECT: the batched copy reading the pinned slot over the bus,
+ * records the slot's event, and returns a ticket.  A slot stays held until
+ * its event has fired.  Slots are used in turn, so when the next one is still
+ * held, submit blocks until the launch holding it (the oldest in flight) has
+ * finished: the wait depends only on the GPU's progress, never on the caller
+ * polling.  A request of more than slot_descs descriptors takes several slots
+ * (one launch each, in order) and its ticket is that of the last.
+ *
+ * Tickets count launches on the ring from 1.  Launches on one stream finish
+ * in order, so ticket t done means every ticket <= t is done; the ring keeps
+ * the highest ticket seen done and answers polls at or below it without
+ * asking the runtime again.  Ticket 0 (what an empty first submit returns)
+ * is always done.
+ *
+ * Descriptors have the meaning, and the disjointness rules, of
+ * tb_batched_copy.  The caller's array is read during tb_ring_submit only and
+ * may be reused on return; the memory the descriptors point at must stay
+ * valid until the ticket is done.  A ring is used by one thread at a time;
+ * tb_ring_submit must be called with the ring's device current.
+ *
+ * tb_ring_create: nslots in [1, 1024], slot_descs in [1, 2^20], flags one of
+ *   TB_RING_STAGED or TB_RING_DIRECT.  *out receives the ring.  Errors:
+ *   TB_ERR_INVALID for a bad argument (checked before any HIP call);
+ *   TB_ERR_NOMEM / TB_ERR_HIP if memory, events or the scratch cannot be had.
+ * tb_ring_submit: n may be 0 (nothing is enqueued; the ticket is that of the
+ *   last launch, or 0).  Every descriptor with bytes > 0 must have non-NULL
+ *   src and dst and neither range may wrap the address space, else
+ *   TB_ERR_INVALID and nothing of the request is enqueued.  TB_ERR_HIP if a
+ *   wait, copy, launch or event record fails; launches of the request made
+ *   before the failure stay enqueued.
+ * tb_ring_poll: *done = 1 if the ticket's launch has finished, else 0.
+ *   TB_ERR_INVALID for a ticket not yet handed out; TB_ERR_HIP if the
+ *   runtime reports an error for the launch.
+ * tb_ring_wait: blocks until the ticket's launch has finished.
+ * tb_ring_destroy: waits for every launch in flight, then frees the ring.
+ *   NULL is a no-op.
+ */
+typedef struct tb_ring tb_ring;
+enum { TB_RING_STAGED = 0, TB_RING_DIRECT = 1 };
+int tb_ring_create(uint32_t nslots, uint32_t slot_descs, uint32_t flags, void *stream, tb_ring **out);
+int tb_ring_submit(tb_ring *ring, const tb_copy_desc *host_desc, uint64_t n, uint64_t *ticket);
+int tb_ring_poll(tb_ring *ring, uint64_t ticket, int32_t *done);
+int tb_ring_wait(tb_ring *ring, uint64_t ticket);
+int tb_ring_destroy(tb_ring *ring);
 
 /*
  * Timing gate (nvbandwidth's spin kernel, "nvbandwidth deep dive" §3.3.1):

@@ -187,6 +187,19 @@ def test_prep_sources_and_gate_argument_checks():
     assert _st("tb_spin_gate_release") == tb.TB_ERR_INVALID                                 # never armed
 
 
+def test_ring_argument_checks():
+    out = ctypes.c_void_p(0x1234)
+    for nslots, slot_descs, flags in ((0, 8, 0), (1025, 8, 0), (2, 0, 0), (2, (1 << 20) + 1, 0), (2, 8, 2),
+                                      (2, 8, 0xFFFFFFFF)):
+        assert _st("tb_ring_create", nslots, slot_descs, flags, None, ctypes.byref(out)) == tb.TB_ERR_INVALID
+    assert _st("tb_ring_create", 2, 8, tb.TB_RING_STAGED, None, None) == tb.TB_ERR_INVALID   # NULL out
+    t, done = ctypes.c_uint64(), ctypes.c_int32()
+    assert _st("tb_ring_submit", None, None, 0, ctypes.byref(t)) == tb.TB_ERR_INVALID       # NULL ring
+    assert _st("tb_ring_poll", None, 0, ctypes.byref(done)) == tb.TB_ERR_INVALID
+    assert _st("tb_ring_wait", None, 0) == tb.TB_ERR_INVALID
+    assert _st("tb_ring_destroy", None) == tb.TB_OK                                          # NULL: no-op
+
+
 def test_product_package_does_not_use_oracle():
     """The HIP package and the oracle share nothing and never import each other."""
     pkg = os.path.join(ROOT, "copy_reduce_amd")
