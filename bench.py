@@ -14,7 +14,8 @@ Default output is ONE JSON line:
                (N+1) x numBytes for the reduce-copy + 2 x sum(bytes) for the batch
   roofline     the dominant kernel (the reduce-copy) against 8 TB/s HBM
   cpu_baseline the oracle timed on one host core over the same step
---suite additionally prints one line per configuration (C1-C5, sweep).
+--suite additionally prints one line per configuration (C1-C5, sweep);
+--cpu-suite times the oracle alone on one host core for every configuration.
 """
 import argparse
 import hashlib
@@ -271,6 +272,36 @@ def cpu_baseline(torch, w, batch, dst, pool):
         "cpu_model": _cpu_model(),
     }
     return cpu, validated
+
+
+def cpu_baseline_suite(args, wl):
+    """The cpu_baseline leg for every configuration: the oracle, as it stands,
+    timed on one host core (median of 3) -- the cumulative reduce over nfloats
+    for C1-C3 and the sweep (rotation does not change the host computation),
+    the per-descriptor memcpy into a 4 GiB host pool image for C4 and C5a.
+    One JSON line per configuration; no GPU work."""
+    import numpy as np
+
+    import oracle
+    common = {"cores": 1, "kind": "oracle", "host_cores_total": os.cpu_count(), "cpu_model": _cpu_model()}
+    works = [wl.REDUCE_CONFIGS[k] for k in ("c1_copy_4MiB_rot", "c2_reduce2_256MiB_rot", "c3_reduce4_64MiB_compress")]
+    works += [wl.sweep_workload(nb, True) for nb in wl.SWEEP_BYTES]
+    for w in works:
+        srcs = [oracle.gen_source(w.nfloats, b, w.fill) for b in range(w.nsrc)]
+        secs = statistics.median([oracle.time_ref_reduce(srcs)[0] for _ in range(3)])
+        rec = {"config": w.name, "nsrc": w.nsrc,
+               "nfloats": w.nfloats, "seconds": round(secs, 6),
+               "gbps": round(w.algorithmic_bytes / secs / 1e9, 3), **common}
+        print(json.dumps({"cpu_suite": rec}), flush=True)
+        del srcs
+    for batch in (wl.batch_c4(), wl.batch_c5()):
+        image = np.full(batch.pool_bytes, wl.POOL_FILL, dtype=np.uint8)
+        secs = statistics.median([oracle.time_ref_batch(image, batch.payload, batch.desc) for _ in range(3)])
+        rec = {"config": batch.name, "ncopies": batch.ncopies, "seconds": round(secs, 6),
+               "gbps": round(batch.algorithmic_bytes / secs / 1e9, 3),
+               "copies_per_s": round(batch.ncopies / secs, 1), **common}
+        print(json.dumps({"cpu_suite": rec}), flush=True)
+        del image
 
 
 def _cpu_model():
@@ -888,6 +919,8 @@ def main():
                          "descriptor) on the same inputs, then exit")
     ap.add_argument("--interference", action="store_true",
                     help="only time C4 (batched, and one call per descriptor) alone and beside a bf16 GEMM, then exit")
+    ap.add_argument("--cpu-suite", action="store_true",
+                    help="only time the oracle on one host core for every configuration (no GPU), then exit")
     ap.add_argument("--ring", action="store_true",
                     help="only time the descriptor-slot ring (host submit/poll cost, end-to-end rate), then exit")
     ap.add_argument("--roofs", action="store_true",
@@ -910,6 +943,10 @@ def main():
     if args.steps < 1 or args.warmup < 0:
         ap.error("--steps must be >= 1 and --warmup >= 0")
 
+    if args.cpu_suite:
+        import workloads as wl
+        cpu_baseline_suite(args, wl)
+        return
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU: the HIP path has no CPU fallback", file=sys.stderr, flush=True)
