@@ -1,6 +1,7 @@
 // Exercises libtb's host-only entry points (slice geometry, rotation, the
 // PrepareReference generators, status strings) and the argument checks of
-// the GPU entry points, which return before any HIP call, in a build with
+// the GPU entry points and of the descriptor-slot ring, which return before
+// any HIP call, in a build with
 // AddressSanitizer and UndefinedBehaviorSanitizer.  Needs no GPU.
 #include <stdint.h>
 #include <stdio.h>
@@ -59,6 +60,19 @@ int main() {
     CHECK(tb_reduce_copy(nullptr, nullptr, 3, 0, nullptr) == TB_OK);
     CHECK(tb_batched_copy(nullptr, 5, nullptr) == TB_ERR_INVALID);
     CHECK(tb_batched_copy(nullptr, 0, nullptr) == TB_OK);
+    tb_ring *ring = nullptr;
+    CHECK(tb_ring_create(0, 8, TB_RING_STAGED, nullptr, &ring) == TB_ERR_INVALID && ring == nullptr);
+    CHECK(tb_ring_create(2, 0, TB_RING_DIRECT, nullptr, &ring) == TB_ERR_INVALID);
+    CHECK(tb_ring_create(1025, 8, TB_RING_STAGED, nullptr, &ring) == TB_ERR_INVALID);
+    CHECK(tb_ring_create(2, (1u << 20) + 1, TB_RING_STAGED, nullptr, &ring) == TB_ERR_INVALID);
+    CHECK(tb_ring_create(2, 8, 7, nullptr, &ring) == TB_ERR_INVALID);
+    CHECK(tb_ring_create(2, 8, TB_RING_STAGED, nullptr, nullptr) == TB_ERR_INVALID);
+    uint64_t ticket = 0;
+    int32_t done = 0;
+    CHECK(tb_ring_submit(nullptr, nullptr, 0, &ticket) == TB_ERR_INVALID);
+    CHECK(tb_ring_poll(nullptr, 0, &done) == TB_ERR_INVALID);
+    CHECK(tb_ring_wait(nullptr, 0) == TB_ERR_INVALID);
+    CHECK(tb_ring_destroy(nullptr) == TB_OK);
     CHECK(tb_batched_set_mode(7) == TB_ERR_INVALID && tb_batched_set_mode(TB_BC_NORMAL) == TB_OK);
     CHECK(tb_prep_sources(nullptr, 64, 0, nullptr, 16, nullptr) == TB_ERR_INVALID);
     CHECK(tb_spin_gate_arm(0, nullptr) == TB_ERR_INVALID);

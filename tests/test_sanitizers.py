@@ -38,7 +38,8 @@ def test_library_host_code_under_sanitizers(tmp_path):
               "-Iinclude", "-Icopy_reduce_amd/csrc", "-c", "copy_reduce_amd/csrc/tb_kernels.hip", "-o", kobj])
     common = ["-std=c++17", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-Iinclude", "-Icopy_reduce_amd/csrc"] + SAN
     objs = []
-    for src in ("copy_reduce_amd/csrc/tb_host.cpp", "copy_reduce_amd/csrc/tb_gen.cpp", "tests/sanitize/host_driver.cpp"):
+    for src in ("copy_reduce_amd/csrc/tb_host.cpp", "copy_reduce_amd/csrc/tb_gen.cpp", "copy_reduce_amd/csrc/tb_ring.cpp",
+                "tests/sanitize/host_driver.cpp"):
         o = str(tmp_path / (os.path.basename(src) + ".o"))
         _run(["g++"] + common + ["-c", src, "-o", o])
         objs.append(o)
