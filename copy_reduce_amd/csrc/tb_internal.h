@@ -96,9 +96,11 @@ uint32_t batched_scanners(uint32_t ncopies, int grid);
 // 1, one more for each launch (their stream orders them).
 // wait_ticks: the longest wait for the queue, in ticks of the device wall
 // clock (normally kBcSealWaitUs).  no_pieces: no wave takes queue pieces, so
-// the recovery copy runs (for tests).
+// the recovery copy runs (for tests).  done_event, if not null, fires when the
+// kernel completes (it is the launch's stop event, not a separate command).
 hipError_t launch_batched_copy(const tb_copy_desc *desc, uint32_t n, BcScratch *scratch, uint64_t epoch,
-                               int cu_count, uint64_t wait_ticks, bool no_pieces, hipStream_t stream);
+                               int cu_count, uint64_t wait_ticks, bool no_pieces, hipStream_t stream,
+                               hipEvent_t done_event = nullptr);
 
 // As launch_batched_copy, for a batch the caller has checked holds no copy
 // longer than kBcSplitAbove: the queue is skipped (no scanner workgroups, no
@@ -106,7 +108,7 @@ hipError_t launch_batched_copy(const tb_copy_desc *desc, uint32_t n, BcScratch *
 // floor.  The launch still clears the scan word of the next epoch, so any
 // launch may follow it on the same scratch.
 hipError_t launch_batched_copy_short(const tb_copy_desc *desc, uint32_t n, BcScratch *scratch, uint64_t epoch,
-                                     int cu_count, hipStream_t stream);
+                                     int cu_count, hipStream_t stream, hipEvent_t done_event = nullptr);
 
 // ---- spin gate ---------------------------------------------------------------
 

@@ -3,6 +3,7 @@
 // Written for CDNA4: wave64, 256 CUs in 8 XCDs, HBM3E.  Nothing here is a
 // contraction, so there is no MFMA; both copies are HBM-bound streams and the
 // design is about keeping enough 16-byte loads in flight per CU.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -696,18 +697,32 @@ uint32_t batched_scanners(uint32_t ncopies, int grid) {
     return s;
 }
 
-hipError_t launch_batched_copy(const tb_copy_desc *desc, uint32_t n, BcScratch *scratch, uint64_t epoch,
-                               int cu_count, uint64_t wait_ticks, bool no_pieces, hipStream_t s) {
-    const int grid = batched_grid(n, cu_count);
-    // pieces of long copies go to as many waves as fit on the chip at once
-    const uint32_t resident = (uint32_t)(cu_count > 0 ? cu_count : 1) * kBcResidentWavesPerCu;
-    hipLaunchKernelGGL(bc_kernel, dim3(grid), dim3(kBcBlock), 0, s, desc, n, scratch, epoch,
-                       batched_scanners(n, grid), wait_ticks, resident, no_pieces ? 1u : 0u);
+// One launch of bc_kernel; with done_event, the event is the launch's own stop
+// event (fired when the kernel completes), which costs no separate command.
+static hipError_t launch_bc(int grid, hipStream_t s, hipEvent_t done_event, const tb_copy_desc *desc, uint32_t n,
+                            BcScratch *scratch, uint64_t epoch, uint32_t scanners, uint64_t wait_ticks,
+                            uint32_t piece_waves, uint32_t no_pieces) {
+    if (done_event != nullptr)
+        hipExtLaunchKernelGGL(bc_kernel, dim3(grid), dim3(kBcBlock), 0, s, nullptr, done_event, 0u, desc, n, scratch,
+                              epoch, scanners, wait_ticks, piece_waves, no_pieces);
+    else
+        hipLaunchKernelGGL(bc_kernel, dim3(grid), dim3(kBcBlock), 0, s, desc, n, scratch, epoch, scanners,
+                           wait_ticks, piece_waves, no_pieces);
     return hipGetLastError();
 }
 
+hipError_t launch_batched_copy(const tb_copy_desc *desc, uint32_t n, BcScratch *scratch, uint64_t epoch,
+                               int cu_count, uint64_t wait_ticks, bool no_pieces, hipStream_t s,
+                               hipEvent_t done_event) {
+    const int grid = batched_grid(n, cu_count);
+    // pieces of long copies go to as many waves as fit on the chip at once
+    const uint32_t resident = (uint32_t)(cu_count > 0 ? cu_count : 1) * kBcResidentWavesPerCu;
+    return launch_bc(grid, s, done_event, desc, n, scratch, epoch, batched_scanners(n, grid), wait_ticks, resident,
+                     no_pieces ? 1u : 0u);
+}
+
 hipError_t launch_batched_copy_short(const tb_copy_desc *desc, uint32_t n, BcScratch *scratch, uint64_t epoch,
-                                     int cu_count, hipStream_t s) {
+                                     int cu_count, hipStream_t s, hipEvent_t done_event) {
     // no scanners and no piece waves: every wave copies its own descriptors
     // and is done; one descriptor per wave, no floor on the grid
     const uint64_t cus = (uint64_t)(cu_count > 0 ? cu_count : 1);
@@ -715,9 +730,7 @@ hipError_t launch_batched_copy_short(const tb_copy_desc *desc, uint32_t n, BcScr
     if (g > cus * kBcMaxGridPerCu)
         g = cus * kBcMaxGridPerCu;
     const int grid = (int)((g + 7) & ~(uint64_t)7);
-    hipLaunchKernelGGL(bc_kernel, dim3(grid), dim3(kBcBlock), 0, s, desc, n, scratch, epoch, 0u, (uint64_t)0, 0u,
-                       0u);
-    return hipGetLastError();
+    return launch_bc(grid, s, done_event, desc, n, scratch, epoch, 0u, 0u, 0u, 0u);
 }
 
 // ============================================================================

@@ -187,17 +187,16 @@ int tb_ring_submit(tb_ring *r, const tb_copy_desc *host_desc, uint64_t n, uint64
         } else {
             read_from = r->host_dev + (size_t)k * r->slot_descs;
         }
-        // the ring sees every length: a slot without long copies skips the queue
+        // The ring sees every length: a slot without long copies skips the
+        // queue.  The slot's event is the launch's own stop event, which saves
+        // the separate record command (about half the host cost of a submit).
         if (any_long)
             e = tbk::launch_batched_copy(read_from, m, r->scratch, t, r->cu_count, wait_ticks,
-                                         mode == TB_BC_NO_PIECES, r->stream);
+                                         mode == TB_BC_NO_PIECES, r->stream, r->event[k]);
         else
-            e = tbk::launch_batched_copy_short(read_from, m, r->scratch, t, r->cu_count, r->stream);
+            e = tbk::launch_batched_copy_short(read_from, m, r->scratch, t, r->cu_count, r->stream, r->event[k]);
         if (e != hipSuccess)
             return tbh::hip_fail(e, "batched-copy launch (ring)");
-        e = hipEventRecord(r->event[k], r->stream);
-        if (e != hipSuccess)
-            return tbh::hip_fail(e, "hipEventRecord(ring slot)");
         r->held_by[k] = t;
         r->next_ticket = t + 1;
     }
