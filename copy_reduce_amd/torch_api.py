@@ -110,9 +110,11 @@ def batched_copy(desc: torch.Tensor, ncopies: Optional[int] = None,
 
 class DescRing:
     """Descriptor-slot ring on the current device: submit host (n, 3) uint64
-    descriptor arrays (absolute src, dst, bytes) and poll their tickets."""
+    descriptor arrays (absolute src, dst, bytes) and poll their tickets.
+    direct: the kernel reads the pinned slots itself (faster in every measured
+    case); otherwise each slot is first copied to device memory."""
 
-    def __init__(self, nslots: int = 32, slot_descs: int = 8192, direct: bool = False,
+    def __init__(self, nslots: int = 32, slot_descs: int = 8192, direct: bool = True,
                  stream: Optional[torch.cuda.Stream] = None):
         self.handle = _tb.tb_ring_create(nslots, slot_descs, _tb.TB_RING_DIRECT if direct else _tb.TB_RING_STAGED,
                                          stream_handle(stream))

@@ -178,13 +178,14 @@ def test_bad_descriptor_rejects_whole_request():
     assert dev.first_mismatch() == -1
 
 
-def test_destroy_waits_for_work_in_flight():
+@pytest.mark.parametrize("direct", [False, True], ids=["staged", "direct"])
+def test_destroy_waits_for_work_in_flight(direct):
     torch = require_gpu()
     from copy_reduce_amd.torch_api import DescRing
     b = wl.batch_c4(seed=4, n=6000, pool_bytes=256 << 20)
     dev = _Dev(torch, b)
-    note("ring destroy with launches in flight")
-    ring = DescRing(nslots=8, slot_descs=1024)
+    note(f"ring destroy with launches in flight direct={direct}")
+    ring = DescRing(nslots=8, slot_descs=1024, direct=direct)
     for a in range(0, b.ncopies, 1000):
         ring.submit(dev.host_desc[a:a + 1000])
     ring.close()                     # no wait before: destroy must wait itself
@@ -211,7 +212,8 @@ def test_recovery_modes_through_ring(mode):
     assert dev.first_mismatch() == -1
 
 
-def test_ring_and_plain_calls_interleave_on_one_stream():
+@pytest.mark.parametrize("direct", [False, True], ids=["staged", "direct"])
+def test_ring_and_plain_calls_interleave_on_one_stream(direct):
     """Ring launches and tb_batched_copy launches on the same stream use
     different scratch and run in stream order."""
     torch = require_gpu()
@@ -221,8 +223,8 @@ def test_ring_and_plain_calls_interleave_on_one_stream():
     dev = _Dev(torch, b)
     dd = torch.from_numpy(dev.host_desc.view(np.int64)).cuda()
     s = torch.cuda.current_stream()
-    note("ring + plain batched copies interleaved")
-    with DescRing(nslots=4, slot_descs=256) as ring:
+    note(f"ring + plain batched copies interleaved direct={direct}")
+    with DescRing(nslots=4, slot_descs=256, direct=direct) as ring:
         t = 0
         for k, a in enumerate(range(0, b.ncopies, 300)):
             m = min(300, b.ncopies - a)
