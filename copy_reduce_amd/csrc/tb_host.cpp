@@ -28,6 +28,11 @@ int hip_fail(hipError_t e, const char *what) {
 
 int batched_mode() { return g_batched_mode.load(std::memory_order_relaxed); }
 
+bool capturing(hipStream_t s) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(s, &st) == hipSuccess && st != hipStreamCaptureStatusNone;
+}
+
 }  // namespace tbh
 
 namespace {
@@ -286,11 +291,13 @@ int tb_batched_copy(const tb_copy_desc *desc_dev, uint32_t ncopies, void *stream
         return TB_OK;
     if (desc_dev == nullptr || (reinterpret_cast<uintptr_t>(desc_dev) & 7u) != 0)
         return TB_ERR_INVALID;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (tbh::capturing(s))
+        return TB_ERR_INVALID;
     DeviceInfo info;
     int rc = device_info(&info);
     if (rc != TB_OK)
         return rc;
-    hipStream_t s = static_cast<hipStream_t>(stream);
     tbk::BcScratch *scratch = nullptr;
     uint64_t epoch = 0;
     rc = scratch_for(s, &scratch, &epoch);

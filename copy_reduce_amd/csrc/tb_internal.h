@@ -129,4 +129,9 @@ int hip_fail(hipError_t e, const char *what);
 // The TB_BC_* mode last set by tb_batched_set_mode.
 int batched_mode();
 
+// True while `s` is being captured into a HIP graph.  The batched copy's
+// launches carry their epoch as a kernel argument, so a replayed capture would
+// reuse one epoch on the scratch: such calls are refused instead.
+bool capturing(hipStream_t s);
+
 }  // namespace tbh

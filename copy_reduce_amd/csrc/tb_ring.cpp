@@ -155,6 +155,8 @@ int tb_ring_create(uint32_t nslots, uint32_t slot_descs, uint32_t flags, void *s
 int tb_ring_submit(tb_ring *r, const tb_copy_desc *host_desc, uint64_t n, uint64_t *ticket) {
     if (r == nullptr || ticket == nullptr || (n > 0 && host_desc == nullptr))
         return TB_ERR_INVALID;
+    if (n > 0 && tbh::capturing(r->stream))
+        return TB_ERR_INVALID;
     // the whole request is checked before any part of it is enqueued
     for (uint64_t i = 0; i < n; i++) {
         const tb_copy_desc &d = host_desc[i];

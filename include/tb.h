@@ -188,8 +188,13 @@ int tb_reduce_copy_ex(float *dst, const float *const *srcs, int32_t nsrc,
  * allocated on the first call for that pair; calls on one stream are ordered,
  * calls on different streams use different scratch (each launch relies on the
  * previous launch on its scratch having finished).
- * Errors: TB_ERR_INVALID for a NULL or misaligned desc_dev with ncopies > 0;
- * TB_ERR_NOMEM if the scratch cannot be allocated; TB_ERR_HIP.
+ * Not for HIP graph capture: each launch is numbered on its scratch when it
+ * is enqueued, and a replayed capture would repeat the number, so a call on a
+ * capturing stream is refused (the reduce-copy has no such state and may be
+ * captured).
+ * Errors: TB_ERR_INVALID for a NULL or misaligned desc_dev with ncopies > 0,
+ * or a stream under capture; TB_ERR_NOMEM if the scratch cannot be
+ * allocated; TB_ERR_HIP.
  */
 int tb_batched_copy(const tb_copy_desc *desc_dev, uint32_t ncopies, void *stream);
 
@@ -248,8 +253,9 @@ int tb_batched_set_mode(int32_t mode);
  *   TB_ERR_NOMEM / TB_ERR_HIP if memory, events or the scratch cannot be had.
  * tb_ring_submit: n may be 0 (nothing is enqueued; the ticket is that of the
  *   last launch, or 0).  Every descriptor with bytes > 0 must have non-NULL
- *   src and dst and neither range may wrap the address space, else
- *   TB_ERR_INVALID and nothing of the request is enqueued.  TB_ERR_HIP if a
+ *   src and dst and neither range may wrap the address space, and the
+ *   ring's stream must not be under graph capture, else TB_ERR_INVALID and
+ *   nothing of the request is enqueued.  TB_ERR_HIP if a
  *   wait, copy, launch or event record fails; launches of the request made
  *   before the failure stay enqueued.
  * tb_ring_poll: *done = 1 if the ticket's launch has finished, else 0.

@@ -280,3 +280,41 @@ def test_shutdown_frees_scratch_and_later_calls_start_afresh():
     tb.tb_spin_gate_release()
     torch.cuda.synchronize()
     assert tb.tb_spin_gate_status() == tb.TB_OK
+
+
+@pytest.mark.filterwarnings("ignore:The CUDA Graph is empty")
+def test_refused_under_graph_capture():
+    """A launch numbers itself on its scratch when enqueued, so a replayed
+    capture would repeat the number: the call is refused on a capturing stream
+    and enqueues nothing; the same calls work once the capture is over."""
+    torch = require_gpu()
+    import copy_reduce_amd as tb
+    from copy_reduce_amd.torch_api import DescRing, make_desc
+    b = wl.batch_random(5, 20, max_bytes=2000, pool_bytes=1 << 20)
+    src = torch.from_numpy(b.payload).cuda()
+    pool = torch.full((b.pool_bytes,), wl.POOL_FILL, dtype=torch.uint8, device="cuda")
+    desc = make_desc(b.desc, int(src.data_ptr()), int(pool.data_ptr()))
+    host = b.desc.astype(np.uint64).copy()
+    host[:, 0] += np.uint64(int(src.data_ptr()))
+    host[:, 1] += np.uint64(int(pool.data_ptr()))
+    torch.cuda.synchronize()
+    note("batched copy refused under graph capture")
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with DescRing(nslots=2, slot_descs=8, stream=side) as ring:
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                with pytest.raises(tb.TBError) as e1:
+                    tb.tb_batched_copy(int(desc.data_ptr()), b.ncopies, side.cuda_stream)
+                with pytest.raises(tb.TBError) as e2:
+                    ring.submit(host)
+        assert e1.value.status == tb.TB_ERR_INVALID and e2.value.status == tb.TB_ERR_INVALID
+        torch.cuda.synchronize()
+        assert bool((pool == wl.POOL_FILL).all())            # nothing ran
+        # the same calls work once the capture is over
+        tb.tb_batched_copy(int(desc.data_ptr()), b.ncopies, side.cuda_stream)
+        side.synchronize()
+    got = pool.cpu().numpy()
+    exp = np.full(b.pool_bytes, wl.POOL_FILL, dtype=np.uint8)
+    oracle.ref_batch(exp, b.payload, b.desc)
+    assert oracle.first_mismatch(got, exp) == -1

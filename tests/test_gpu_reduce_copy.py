@@ -205,3 +205,34 @@ def test_reduce_copy_invalid_args_enqueue_nothing():
     assert tb.lib.tb_reduce_copy(dst.ptr, arr, 1, n, None) == tb.TB_ERR_INVALID
     torch.cuda.synchronize()
     assert np.all(dst.download() == 0x33)
+
+
+@pytest.mark.parametrize("nsrc", [1, 3])
+def test_reduce_copy_captured_in_a_graph_replays_exactly(nsrc):
+    """The reduce-copy keeps no state between launches, so it may be captured
+    into a HIP graph.  The graph is replayed three times, with the destination
+    overwritten eagerly and the device synchronised between replays; every
+    replay must give the oracle's bytes."""
+    torch = require_gpu()
+    import copy_reduce_amd as tb
+    n = (1 << 18) + 5
+    note(f"reduce_copy graph capture nsrc={nsrc} n={n}")
+    srcs = _sources(nsrc, n)
+    sbufs = [DevBuf(torch, n * 4, 4 * b).upload(s) for b, s in enumerate(srcs)]
+    dbuf = DevBuf(torch, n * 4, 0)
+    exp = oracle.ref_reduce(srcs, n=n)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            tb.tb_reduce_copy(dbuf.ptr, [b.ptr for b in sbufs], n, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        dbuf.t[dbuf.start:dbuf.start + n * 4].fill_(0x5A + rep)       # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = dbuf.download().view(np.float32)
+        assert oracle.first_mismatch(got, exp) == -1, f"replay {rep}"
+        assert dbuf.guards_intact()
