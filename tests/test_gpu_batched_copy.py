@@ -318,3 +318,43 @@ def test_refused_under_graph_capture():
     exp = np.full(b.pool_bytes, wl.POOL_FILL, dtype=np.uint8)
     oracle.ref_batch(exp, b.payload, b.desc)
     assert oracle.first_mismatch(got, exp) == -1
+
+
+def test_threads_on_their_own_streams():
+    """Four host threads, each on its own stream with its own batch and pool,
+    call tb_batched_copy concurrently (the library's scratch map is shared and
+    locked; each stream gets its own scratch)."""
+    import threading
+    torch = require_gpu()
+    import copy_reduce_amd as tb
+    from copy_reduce_amd.torch_api import make_desc
+    jobs = []
+    for t in range(4):
+        b = wl.batch_c5(seed=40 + t, pool_bytes=64 << 20, n_block=400, n_index=100, n_mla=1)
+        src = torch.from_numpy(b.payload).cuda()
+        pool = torch.full((b.pool_bytes,), wl.POOL_FILL, dtype=torch.uint8, device="cuda")
+        desc = make_desc(b.desc, int(src.data_ptr()), int(pool.data_ptr()))
+        jobs.append((b, src, pool, desc, torch.cuda.Stream()))
+    torch.cuda.synchronize()
+    note("batched copy from 4 threads on 4 streams")
+    errors = []
+
+    def work(job):
+        b, _, _, desc, s = job
+        try:
+            for _ in range(5):
+                tb.tb_batched_copy(int(desc.data_ptr()), b.ncopies, s.cuda_stream)
+            s.synchronize()
+        except Exception as e:  # reported below, in the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=work, args=(j,)) for j in jobs]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    for b, _, pool, _, _ in jobs:
+        exp = np.full(b.pool_bytes, wl.POOL_FILL, dtype=np.uint8)
+        oracle.ref_batch(exp, b.payload, b.desc)
+        assert oracle.first_mismatch(pool.cpu().numpy(), exp) == -1
