@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
+import workloads as wl
 from gpu_util import GUARD_BYTE, DevBuf, note, require_gpu
 
 pytestmark = pytest.mark.gpu
@@ -80,3 +81,42 @@ def test_reduce2_above_4GiB_sampled():
         exp = oracle.ref_reduce([fa[lo:hi].cpu().numpy(), fb[lo:hi].cpu().numpy()])
         assert oracle.first_mismatch(got, exp) == -1, f"window at element {lo}"
     assert _guards_on_device(dst)
+
+
+def test_batched_copy_millions_of_descriptors():
+    """4,500,000 copies of 1-48 bytes at arbitrary alignments plus three long
+    copies: more descriptors than the largest grid has waves times 64, so every
+    wave walks several 64-descriptor blocks, and thousands of scanner
+    workgroups publish.  Compared with the oracle byte for byte."""
+    import copy_reduce_amd as tb
+    from copy_reduce_amd.torch_api import make_desc
+    torch = require_gpu()
+    rng = np.random.default_rng(77)
+    n_small, MiB = 4_500_000, 1 << 20
+    sizes = rng.integers(1, 49, size=n_small).astype(np.int64)
+    long_sizes = np.array([3 * MiB + 5, MiB, 200_000], np.int64)
+    sizes = np.concatenate([long_sizes[:1], sizes[:n_small // 2], long_sizes[1:2], sizes[n_small // 2:], long_sizes[2:]])
+    n = sizes.size
+    # sources packed with 0-15 bytes of slack; destinations packed in a shuffled order with 0-7 bytes of slack
+    src_off = np.cumsum(np.concatenate([[0], sizes[:-1] + rng.integers(0, 16, size=n - 1)])).astype(np.int64)
+    order = rng.permutation(n)
+    gaps = rng.integers(0, 8, size=n)
+    dst_sorted = np.cumsum(np.concatenate([[0], (sizes[order] + gaps[order])[:-1]])).astype(np.int64)
+    dst_off = np.empty(n, np.int64)
+    dst_off[order] = dst_sorted
+    src_bytes = int(src_off[-1] + sizes[-1])
+    pool_bytes = int(dst_off.max() + sizes.max() + 64)
+    desc = np.stack([src_off, dst_off, sizes], axis=1).astype(np.uint64)
+    batch = wl.Batch("millions", desc, src_bytes, pool_bytes, 77, payload=wl.random_payload(rng, src_bytes))
+    info = tb.tb_launch_info(0, 1, n)
+    note(f"max size: batched copy of {n} descriptors, grid {info['batched_blocks']} workgroups")
+    assert n > 64 * 4 * info["batched_blocks"]
+    src = torch.from_numpy(batch.payload).cuda()
+    pool = torch.full((pool_bytes,), wl.POOL_FILL, dtype=torch.uint8, device="cuda")
+    d = make_desc(desc, int(src.data_ptr()), int(pool.data_ptr()))
+    torch.cuda.synchronize()
+    tb.tb_batched_copy(int(d.data_ptr()), n, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    exp = np.full(pool_bytes, wl.POOL_FILL, dtype=np.uint8)
+    oracle.ref_batch(exp, batch.payload, desc)
+    assert oracle.first_mismatch(pool.cpu().numpy(), exp) == -1
