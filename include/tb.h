@@ -187,7 +187,9 @@ int tb_reduce_copy_ex(float *dst, const float *const *srcs, int32_t nsrc,
  * The kernel uses a small library-owned scratch area per (device, stream),
  * allocated on the first call for that pair; calls on one stream are ordered,
  * calls on different streams use different scratch (each launch relies on the
- * previous launch on its scratch having finished).
+ * previous launch on its scratch having finished).  The scratch is found by
+ * the stream's handle: synchronise a stream before destroying it if a new
+ * stream could be created with the same handle while its copy still runs.
  * Not for HIP graph capture: each launch is numbered on its scratch when it
  * is enqueued, and a replayed capture would repeat the number, so a call on a
  * capturing stream is refused (the reduce-copy has no such state and may be
