@@ -6,8 +6,9 @@ One step = one pass of the whole hot path over one batch of synthetic input:
   2. the two-source fp32 reduce-copy over 256 MiB buffers (tb_reduce_copy),
   3. the 47,520-copy batched scattered copy into a 4 GiB pool (tb_batched_copy),
 all enqueued on one stream.  Inputs are prepared (and resident in HBM) before
-the timed region; K steps are enqueued behind the spin gate with a HIP event
-at every kernel boundary, so each launch is timed on the stream it runs on.
+the timed region; K steps are enqueued behind the spin gate between two HIP
+events (the value), then enqueued again with every launch carrying its own
+start and stop event (per-kernel times, on the stream each launch runs on).
 
 Default output is ONE JSON line:
   value        whole-step throughput, algorithmic HBM GB/s (decimal):
@@ -78,6 +79,47 @@ class Timed:
             raise RuntimeError("spin gate timed out: the timed launches were not gated")
         ms = [evs[j].elapsed_time(evs[j + 1]) for j in range(len(launches))]
         return ms, evs[0].elapsed_time(evs[-1]), wall
+
+
+def run_whole(torch, tb, stream, launches):
+    """The launches behind the spin gate with one event before the first and
+    one after the last (nvbandwidth's protocol): (ms, wall seconds)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    tb.tb_spin_gate_arm(GATE_TIMEOUT_MS, stream.cuda_stream)
+    e0.record(stream)
+    for fn in launches:
+        fn()
+    e1.record(stream)
+    tb.tb_spin_gate_release()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if tb.tb_spin_gate_status() != tb.TB_OK:
+        raise RuntimeError("spin gate timed out: the timed launches were not gated")
+    return e0.elapsed_time(e1), wall
+
+
+def run_launch_events(torch, tb, stream, launches):
+    """The launches behind the spin gate, each carrying its own start and stop
+    event (tb_time_next_launch), so no event command sits between kernels:
+    (per-launch ms, ms from the first start to the last stop)."""
+    def made():
+        evs = [torch.cuda.Event(enable_timing=True) for _ in launches]
+        for e in evs:                  # a first record creates the underlying event
+            e.record(stream)
+        return evs
+    st, sp = made(), made()
+    torch.cuda.synchronize()
+    tb.tb_spin_gate_arm(GATE_TIMEOUT_MS, stream.cuda_stream)
+    for j, fn in enumerate(launches):
+        tb.tb_time_next_launch(st[j].cuda_event, sp[j].cuda_event)
+        fn()
+    tb.tb_spin_gate_release()
+    torch.cuda.synchronize()
+    if tb.tb_spin_gate_status() != tb.TB_OK:
+        raise RuntimeError("spin gate timed out: the timed launches were not gated")
+    return [st[j].elapsed_time(sp[j]) for j in range(len(launches))], st[0].elapsed_time(sp[-1])
 
 
 def device_record(torch, tb):
@@ -174,7 +216,10 @@ def main_line(args, torch, tb, wl):
     launches = []
     for i in range(args.steps):
         launches += [rc(i), bc(i)]
-    ms, total_ms, wall = Timed(torch, tb, stream).run(launches)
+    # the K steps as one timed region (the value), then the same K steps again
+    # with each launch carrying its own events (the per-kernel figures)
+    total_ms, wall = run_whole(torch, tb, stream, launches)
+    ms, total_ms_launch_events = run_launch_events(torch, tb, stream, launches)
     rc_ms, bc_ms = ms[0::2], ms[1::2]
 
     rc_bytes, bc_bytes = w.algorithmic_bytes, batch.algorithmic_bytes
@@ -230,6 +275,13 @@ def main_line(args, torch, tb, wl):
             "traffic": traffic,
         },
         "wall_s_timed_region": round(wall, 4),
+        "timing": {
+            "value": "HIP events before the first and after the last of the K timed steps, behind a spin "
+                     "kernel (nvbandwidth's protocol)",
+            "parts_and_roofline": "the same K steps again, each launch carrying its own start and stop event "
+                                  "(hipExtLaunchKernel launch events), on the launch stream",
+            "ms_per_step_with_launch_events": round(total_ms_launch_events / args.steps, 4),
+        },
     }
 
     if not args.no_cpu_baseline:
@@ -319,6 +371,15 @@ def _cpu_model():
 # --suite: every configuration, one JSON line each
 # ---------------------------------------------------------------------------
 
+def _kernel_and_loop(nbytes, kernel_ms, whole_ms, steps):
+    """Two more readings of the same launches: each kernel's own duration
+    (launch-carried events) and the loop's rate with events at its two ends."""
+    kg = nbytes / (kernel_ms * 1e-3) / 1e9
+    lg = steps * nbytes / (whole_ms * 1e-3) / 1e9
+    return {"ms_kernel": round(kernel_ms, 5), "kernel_frac_of_peak": round(kg / HBM_PEAK_GBPS, 4),
+            "loop_ms_per_launch": round(whole_ms / steps, 5), "loop_frac_of_peak": round(lg / HBM_PEAK_GBPS, 4)}
+
+
 def suite(args, torch, tb, wl):
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
@@ -351,7 +412,9 @@ def suite(args, torch, tb, wl):
                 ptrs, dp = rs.pointers(i), dptr_for(i)
                 launches.append(lambda p=ptrs, dp=dp: tb.tb_reduce_copy(dp, p, w.nfloats, sh))
             ms, total, _ = timer.run(launches)
-            means.append((statistics.mean(ms), min(ms), max(ms), total))
+            kms, _ = run_launch_events(torch, tb, stream, launches)
+            whole, _ = run_whole(torch, tb, stream, launches)
+            means.append((statistics.mean(ms), min(ms), max(ms), total, statistics.mean(kms), whole))
         med = sorted(means)[len(means) // 2]
         gbps = w.algorithmic_bytes / (med[0] * 1e-3) / 1e9
         out = {"config": w.name + ("_dstrot" if rotate_dst else ""), "nsrc": w.nsrc, "nfloats": w.nfloats,
@@ -360,6 +423,7 @@ def suite(args, torch, tb, wl):
                "ms_cold": round(cold_ms[0], 5),
                "gbps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
                "aggregate_gbps": round(args.steps * w.algorithmic_bytes / (med[3] * 1e-3) / 1e9, 1)}
+        out.update(_kernel_and_loop(w.algorithmic_bytes, med[4], med[5], args.steps))
         del rs, dst, dsts
         torch.cuda.empty_cache()
         return out
@@ -377,12 +441,15 @@ def suite(args, torch, tb, wl):
             d = batch_desc_for(tb, b, i)
             launches.append(lambda d=d: tb.tb_batched_copy(int(d.data_ptr()), batch.ncopies, sh))
         ms, total, _ = timer.run(launches)
+        kms, _ = run_launch_events(torch, tb, stream, launches)
+        whole, _ = run_whole(torch, tb, stream, launches)
         mean = statistics.mean(ms)
         gbps = batch.algorithmic_bytes / (mean * 1e-3) / 1e9
         out = {"config": f"{batch.name}_{tag}", "ncopies": batch.ncopies, "payload_bytes": batch.total_bytes,
                "replicas": b["kb"], "ms_mean": round(mean, 5), "ms_min": round(min(ms), 5),
                "ms_max": round(max(ms), 5), "ms_cold": round(cold_ms[0], 5), "gbps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
                "copies_per_s": round(batch.ncopies / (mean * 1e-3), 1)}
+        out.update(_kernel_and_loop(batch.algorithmic_bytes, statistics.mean(kms), whole, args.steps))
         del b
         torch.cuda.empty_cache()
         return out

@@ -313,6 +313,11 @@ int tb_batched_copy(const tb_copy_desc *desc_dev, uint32_t ncopies, void *stream
     return TB_OK;
 }
 
+int tb_time_next_launch(void *start_event, void *stop_event) {
+    tbk::set_next_launch_events(static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event));
+    return TB_OK;
+}
+
 int tb_spin_gate_arm(uint32_t timeout_ms, void *stream) {
     if (timeout_ms == 0 || timeout_ms > 60000)
         return TB_ERR_INVALID;

@@ -110,6 +110,13 @@ hipError_t launch_batched_copy(const tb_copy_desc *desc, uint32_t n, BcScratch *
 hipError_t launch_batched_copy_short(const tb_copy_desc *desc, uint32_t n, BcScratch *scratch, uint64_t epoch,
                                      int cu_count, hipStream_t stream, hipEvent_t done_event = nullptr);
 
+// ---- launch events -------------------------------------------------------------
+
+// The next kernel launched by the calling host thread records `start` when it
+// begins and `stop` when it completes, as part of the launch (either may be
+// null).  Consumed by that launch.
+void set_next_launch_events(hipEvent_t start, hipEvent_t stop);
+
 // ---- spin gate ---------------------------------------------------------------
 
 // One thread waits until *flag != 0, or until timeout_ticks of the device

@@ -249,13 +249,37 @@ int reduce_grid(uint64_t nfloats, int nsrc, bool vector_path, int cu_count) {
     return (int)(g > 0 ? g : 8);
 }
 
+// Events the next launch made by this host thread records as part of the
+// launch itself (set by tb_time_next_launch; consumed by that launch).
+static thread_local hipEvent_t t_next_start = nullptr;
+static thread_local hipEvent_t t_next_stop = nullptr;
+
+void set_next_launch_events(hipEvent_t start, hipEvent_t stop) {
+    t_next_start = start;
+    t_next_stop = stop;
+}
+
+// Every kernel of the library is launched here.  With events (the timing hook,
+// or `done` from the caller), the launch carries them as its own start / stop
+// events, so no separate event command sits between kernels.
+template <typename... KArgs, typename... Args>
+static hipError_t launch(void (*kernel)(KArgs...), int grid, int block, hipStream_t s, hipEvent_t done,
+                         Args... args) {
+    const hipEvent_t start = t_next_start;
+    const hipEvent_t stop = done != nullptr ? done : t_next_stop;
+    t_next_start = t_next_stop = nullptr;
+    if (start != nullptr || stop != nullptr)
+        hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(block), 0, s, start, stop, 0u, args...);
+    else
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(block), 0, s, args...);
+    return hipGetLastError();
+}
+
 template <int N>
 static hipError_t launch_n(const ReduceArgs &a, bool vector_path, int grid, hipStream_t s) {
     if (vector_path)
-        hipLaunchKernelGGL(rc_vec_kernel<N>, dim3(grid), dim3(kRcBlock), 0, s, a);
-    else
-        hipLaunchKernelGGL(rc_scalar_kernel<N>, dim3(grid), dim3(kRcBlock), 0, s, a);
-    return hipGetLastError();
+        return launch(rc_vec_kernel<N>, grid, kRcBlock, s, nullptr, a);
+    return launch(rc_scalar_kernel<N>, grid, kRcBlock, s, nullptr, a);
 }
 
 hipError_t launch_reduce_copy(const ReduceArgs &a, int nsrc, bool vector_path, int cu_count,
@@ -263,8 +287,7 @@ hipError_t launch_reduce_copy(const ReduceArgs &a, int nsrc, bool vector_path, i
     const int grid = reduce_grid(a.n, nsrc, vector_path, cu_count);
     switch (nsrc) {
     case 0:
-        hipLaunchKernelGGL(rc_memset_kernel, dim3(grid), dim3(kRcBlock), 0, s, a);
-        return hipGetLastError();
+        return launch(rc_memset_kernel, grid, kRcBlock, s, nullptr, a);
     case 1: return launch_n<1>(a, vector_path, grid, s);
     case 2: return launch_n<2>(a, vector_path, grid, s);
     case 3: return launch_n<3>(a, vector_path, grid, s);
@@ -702,13 +725,8 @@ uint32_t batched_scanners(uint32_t ncopies, int grid) {
 static hipError_t launch_bc(int grid, hipStream_t s, hipEvent_t done_event, const tb_copy_desc *desc, uint32_t n,
                             BcScratch *scratch, uint64_t epoch, uint32_t scanners, uint64_t wait_ticks,
                             uint32_t piece_waves, uint32_t no_pieces) {
-    if (done_event != nullptr)
-        hipExtLaunchKernelGGL(bc_kernel, dim3(grid), dim3(kBcBlock), 0, s, nullptr, done_event, 0u, desc, n, scratch,
-                              epoch, scanners, wait_ticks, piece_waves, no_pieces);
-    else
-        hipLaunchKernelGGL(bc_kernel, dim3(grid), dim3(kBcBlock), 0, s, desc, n, scratch, epoch, scanners,
-                           wait_ticks, piece_waves, no_pieces);
-    return hipGetLastError();
+    return launch(bc_kernel, grid, kBcBlock, s, done_event, desc, n, scratch, epoch, scanners, wait_ticks,
+                  piece_waves, no_pieces);
 }
 
 hipError_t launch_batched_copy(const tb_copy_desc *desc, uint32_t n, BcScratch *scratch, uint64_t epoch,
@@ -754,8 +772,7 @@ __global__ void spin_gate_kernel(const uint32_t *flag, uint32_t *timed_out, uint
 
 hipError_t launch_spin_gate(const uint32_t *flag, uint32_t *timed_out, uint64_t timeout_ticks,
                             hipStream_t s) {
-    hipLaunchKernelGGL(spin_gate_kernel, dim3(1), dim3(64), 0, s, flag, timed_out, timeout_ticks);
-    return hipGetLastError();
+    return launch(spin_gate_kernel, 1, 64, s, nullptr, flag, timed_out, timeout_ticks);
 }
 
 }  // namespace tbk

@@ -276,6 +276,19 @@ int tb_ring_wait(tb_ring *ring, uint64_t ticket);
 int tb_ring_destroy(tb_ring *ring);
 
 /*
+ * Timing hook: the next kernel the calling thread launches through this
+ * library (any entry point, the spin gate included) records start_event when
+ * it begins and stop_event when it completes.  The events travel with the
+ * launch (hipExtLaunchKernel's launch events) instead of being separate
+ * commands between kernels, which on MI355X add about 3 us per launch to a
+ * back-to-back sequence.  Either event may be NULL (a hipEvent_t created by
+ * the caller, with timing enabled to read elapsed times).  One launch only;
+ * a call that fails before launching leaves the hook set for the next.
+ * Always TB_OK.
+ */
+int tb_time_next_launch(void *start_event, void *stop_event);
+
+/*
  * Timing gate (nvbandwidth's spin kernel, "nvbandwidth deep dive" §3.3.1):
  * tb_spin_gate_arm enqueues on `stream` a one-thread kernel that waits until
  * tb_spin_gate_release() is called, so that work queued behind it starts back

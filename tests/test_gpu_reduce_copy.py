@@ -236,3 +236,28 @@ def test_reduce_copy_captured_in_a_graph_replays_exactly(nsrc):
         got = dbuf.download().view(np.float32)
         assert oracle.first_mismatch(got, exp) == -1, f"replay {rep}"
         assert dbuf.guards_intact()
+
+
+def test_time_next_launch_events_travel_with_one_launch():
+    """tb_time_next_launch: the next launch records the two events itself; the
+    launch after it leaves them alone."""
+    torch = require_gpu()
+    import copy_reduce_amd as tb
+    n = 1 << 24                                   # 64 MiB: at least 16 us at 8 TB/s
+    note(f"timing hook on a one-source copy n={n}")
+    src = torch.arange(n, dtype=torch.float32, device="cuda")
+    dst = torch.zeros(n, dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream()
+    st, sp = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st.record(s)
+    sp.record(s)
+    torch.cuda.synchronize()
+    tb.tb_time_next_launch(st.cuda_event, sp.cuda_event)
+    tb.tb_reduce_copy(int(dst.data_ptr()), [int(src.data_ptr())], n, s.cuda_stream)
+    torch.cuda.synchronize()
+    t = st.elapsed_time(sp)
+    assert 0.0167 <= t < 50.0, t
+    assert torch.equal(dst, src)
+    tb.tb_reduce_copy(int(dst.data_ptr()), [int(src.data_ptr())], n, s.cuda_stream)   # hook consumed
+    torch.cuda.synchronize()
+    assert st.elapsed_time(sp) == t
