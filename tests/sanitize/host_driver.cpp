@@ -73,6 +73,7 @@ int main() {
     CHECK(tb_ring_poll(nullptr, 0, &done) == TB_ERR_INVALID);
     CHECK(tb_ring_wait(nullptr, 0) == TB_ERR_INVALID);
     CHECK(tb_ring_destroy(nullptr) == TB_OK);
+    CHECK(tb_time_next_launch(nullptr, nullptr) == TB_OK);
     CHECK(tb_batched_set_mode(7) == TB_ERR_INVALID && tb_batched_set_mode(TB_BC_NORMAL) == TB_OK);
     CHECK(tb_prep_sources(nullptr, 64, 0, nullptr, 16, nullptr) == TB_ERR_INVALID);
     CHECK(tb_spin_gate_arm(0, nullptr) == TB_ERR_INVALID);

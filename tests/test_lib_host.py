@@ -171,6 +171,12 @@ def test_batched_copy_argument_checks():
     assert _st("tb_batched_copy", None, 0, None) == tb.TB_OK
 
 
+def test_timing_hook_needs_no_device():
+    assert _st("tb_time_next_launch", None, None) == tb.TB_OK
+    assert _st("tb_time_next_launch", 0x1234, None) == tb.TB_OK      # stored only; consumed by a launch
+    assert _st("tb_time_next_launch", None, None) == tb.TB_OK        # cleared again
+
+
 def test_batched_mode_hook_checks():
     for bad in (-1, 3, 1 << 20):
         assert _st("tb_batched_set_mode", bad) == tb.TB_ERR_INVALID
