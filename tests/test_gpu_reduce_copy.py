@@ -248,15 +248,18 @@ def test_time_next_launch_events_travel_with_one_launch():
     src = torch.arange(n, dtype=torch.float32, device="cuda")
     dst = torch.zeros(n, dtype=torch.float32, device="cuda")
     s = torch.cuda.current_stream()
-    st, sp = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st, sp, ref = (torch.cuda.Event(enable_timing=True) for _ in range(3))
     st.record(s)
     sp.record(s)
+    ref.record(s)                                 # later than both first records
     torch.cuda.synchronize()
     tb.tb_time_next_launch(st.cuda_event, sp.cuda_event)
     tb.tb_reduce_copy(int(dst.data_ptr()), [int(src.data_ptr())], n, s.cuda_stream)
     torch.cuda.synchronize()
+    assert ref.elapsed_time(st) > 0.0             # both were recorded again, by the launch
+    assert ref.elapsed_time(sp) > ref.elapsed_time(st)
     t = st.elapsed_time(sp)
-    assert 0.0 < t < 50.0, t                      # the events now bracket the copy, not the first records
+    assert 0.0 < t < 50.0, t
     assert torch.equal(dst, src)
     tb.tb_reduce_copy(int(dst.data_ptr()), [int(src.data_ptr())], n, s.cuda_stream)   # hook consumed
     torch.cuda.synchronize()
