@@ -688,9 +688,11 @@ def cache_study(args, torch, tb, wl):
 
 def interference(args, torch, tb, wl):
     """A bf16 GEMM stream on a second stream (default priority) while C4 runs:
-    the batched launch and one hipMemcpyAsync per descriptor, each alone and
-    under the GEMM, and the GEMM's own slowdown.  Mooncake RFC #5041
-    (Motivation) reports per-call copies collapsing under such a GEMM."""
+    batched launches back to back for as long as the GEMMs run (uncapped, and
+    with the grid capped at 2,048 / 512 / 128 / 32 workgroups), and one
+    hipMemcpyAsync per descriptor; the slowdown of each side.  Mooncake RFC
+    #5041 (Motivation; Design of #5040, interference with compute) reports
+    per-call copies collapsing under such a GEMM and asks about CU budgets."""
     import numpy as np
 
     s_copy = torch.cuda.current_stream()
@@ -732,14 +734,46 @@ def interference(args, torch, tb, wl):
         ms, _, _ = timer.run([lambda d=d: tb.tb_batched_copy(int(d.data_ptr()), batch.ncopies, sh) for d in ds])
         return statistics.mean(ms)
 
-    alone_ms = copies()
-    ng = max(4, int(round(4 * alone_ms * (args.steps + args.warmup) / gemm_ms)) + 4)
-    torch.cuda.synchronize()
-    g0, g1 = gemms(ng)
-    under_ms = copies()
-    torch.cuda.synchronize()
-    gemm_under_ms = g0.elapsed_time(g1) / ng
-    ok_batched = batch_sample_check(torch, b["pool"], batch, b["src"])
+    def overlap(cap):
+        """Batched copies back to back on the copy stream for as long as 10
+        GEMMs run on the GEMM stream: both slowdowns against fresh runs alone."""
+        tb.tb_batched_set_max_workgroups(cap)
+        a_ms = copies()
+        e0, e1 = gemms(10)
+        torch.cuda.synchronize()
+        g_alone = e0.elapsed_time(e1) / 10
+        m = int(1.2 * 10 * g_alone / a_ms) + 2
+        ds = [batch_desc_for(tb, b, i) for i in range(m)]
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        h0, h1 = gemms(10)
+        c0.record(s_copy)
+        for d in ds:
+            tb.tb_batched_copy(int(d.data_ptr()), batch.ncopies, sh)
+        c1.record(s_copy)
+        torch.cuda.synchronize()
+        g_under = h0.elapsed_time(h1) / 10
+        c_window = c0.elapsed_time(c1)
+        c_under = c_window / m
+        e0, e1 = gemms(10)               # alone again after: the baseline is the faster of the two
+        torch.cuda.synchronize()
+        g_alone = min(g_alone, e0.elapsed_time(e1) / 10)
+        return {"max_workgroups": cap or "none", "copies": m,
+                "us_alone": round(a_ms * 1e3, 2), "us_under_gemm": round(c_under * 1e3, 2),
+                "copy_slowdown": round(c_under / a_ms, 3),
+                "gbps_alone": round(batch.algorithmic_bytes / (a_ms * 1e-3) / 1e9, 1),
+                "gbps_under_gemm": round(batch.algorithmic_bytes / (c_under * 1e-3) / 1e9, 1),
+                "gemm_ms_alone": round(g_alone, 4), "gemm_ms_under_copies": round(g_under, 4),
+                "gemm_slowdown": round(g_under / g_alone, 3),
+                "copy_window_over_gemm_window": round(c_window / (g_under * 10), 2),
+                "validated_sample": batch_sample_check(torch, b["pool"], batch, b["src"])}
+
+    runs = []
+    try:
+        for cap in (0, 2048, 512, 128, 32):
+            runs.append(overlap(cap))
+    finally:
+        tb.tb_batched_set_max_workgroups(0)
 
     # one hipMemcpyAsync per descriptor, the first 2,000 descriptors of C4
     memcpy = hip_memcpy_fn()
@@ -770,13 +804,8 @@ def interference(args, torch, tb, wl):
                      for s, d, n in sub[::50])
     rec = {
         "gemm": {"shape": [M, M, M], "dtype": "bf16", "ms_alone": round(gemm_ms, 4),
-                 "tflops_alone": round(flop / (gemm_ms * 1e-3) / 1e12, 1),
-                 "ms_under_batched_copies": round(gemm_under_ms, 4),
-                 "slowdown": round(gemm_under_ms / gemm_ms, 3)},
-        "batched_copy_c4": {"us_alone": round(alone_ms * 1e3, 2), "us_under_gemm": round(under_ms * 1e3, 2),
-                            "slowdown": round(under_ms / alone_ms, 3),
-                            "gbps_under_gemm": round(batch.algorithmic_bytes / (under_ms * 1e-3) / 1e9, 1),
-                            "validated_sample": ok_batched},
+                 "tflops_alone": round(flop / (gemm_ms * 1e-3) / 1e12, 1)},
+        "batched_copy_c4_beside_gemm": runs,
         "per_call_hipMemcpyAsync_2000_of_c4": {
             "ms_alone": round(pc_alone * 1e3, 3), "ms_under_gemm": round(pc_under * 1e3, 3),
             "slowdown": round(pc_under / pc_alone, 3),

@@ -14,5 +14,5 @@ from ._tb import (  # noqa: F401
     TBError, lib, tb_batched_copy, tb_batched_set_mode, tb_launch_info, tb_num_slices, tb_prep_reference, tb_prep_sources,
     tb_reduce_copy, tb_ring_create, tb_ring_destroy, tb_ring_poll, tb_ring_submit, tb_ring_wait, tb_rotate_sources,
     tb_shutdown, tb_slice_stride, tb_spin_gate_arm, tb_spin_gate_release, tb_spin_gate_status, tb_status_string,
-    tb_time_next_launch,
+    tb_time_next_launch, tb_batched_set_max_workgroups,
 )

@@ -27,7 +27,7 @@ EXPORTS = (
     "tb_reduce_copy_ex", "tb_batched_copy", "tb_batched_set_mode", "tb_spin_gate_arm", "tb_spin_gate_release",
     "tb_spin_gate_status", "tb_launch_info", "tb_shutdown",
     "tb_ring_create", "tb_ring_submit", "tb_ring_poll", "tb_ring_wait", "tb_ring_destroy",
-    "tb_time_next_launch",
+    "tb_time_next_launch", "tb_batched_set_max_workgroups",
 )
 
 # torch ships its own HIP runtime under the same soname (libamdhip64.so.7) as
@@ -80,6 +80,7 @@ _SIGS = {
     "tb_ring_wait": (ctypes.c_int, [_vp, _u64]),
     "tb_ring_destroy": (ctypes.c_int, [_vp]),
     "tb_time_next_launch": (ctypes.c_int, [_vp, _vp]),
+    "tb_batched_set_max_workgroups": (ctypes.c_int, [_u32]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(lib, _name)
@@ -196,6 +197,10 @@ def tb_batched_set_mode(mode: int) -> None:
 def tb_time_next_launch(start_event: int, stop_event: int) -> None:
     """The next launch this thread makes records these events (hipEvent_t handles, 0 for none)."""
     _check("tb_time_next_launch", lib.tb_time_next_launch(start_event or None, stop_event or None))
+
+
+def tb_batched_set_max_workgroups(max_workgroups: int) -> None:
+    _check("tb_batched_set_max_workgroups", lib.tb_batched_set_max_workgroups(max_workgroups))
 
 
 def tb_spin_gate_arm(timeout_ms: int, stream: int) -> None:

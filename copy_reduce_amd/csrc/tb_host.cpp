@@ -286,6 +286,11 @@ int tb_batched_set_mode(int32_t mode) {
     return TB_OK;
 }
 
+int tb_batched_set_max_workgroups(uint32_t max_workgroups) {
+    tbk::set_batched_max_workgroups(max_workgroups);
+    return TB_OK;
+}
+
 int tb_batched_copy(const tb_copy_desc *desc_dev, uint32_t ncopies, void *stream) {
     if (ncopies == 0)
         return TB_OK;

@@ -89,6 +89,8 @@ struct BcScratch {
 constexpr size_t kBcScratchBytes = sizeof(BcScratch);
 
 int batched_grid(uint32_t ncopies, int cu_count);
+// Cap every later batched-copy launch at max_wgs workgroups (0: no cap).
+void set_batched_max_workgroups(uint32_t max_wgs);
 uint32_t batched_scanners(uint32_t ncopies, int grid);
 
 // Enqueue the batched copy.  `scratch` must be kBcScratchBytes of device

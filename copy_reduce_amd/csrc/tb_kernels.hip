@@ -3,6 +3,8 @@
 // Written for CDNA4: wave64, 256 CUs in 8 XCDs, HBM3E.  Nothing here is a
 // contraction, so there is no MFMA; both copies are HBM-bound streams and the
 // design is about keeping enough 16-byte loads in flight per CU.
+#include <atomic>
+
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -700,6 +702,23 @@ __global__ __launch_bounds__(kBcBlock, kBcBlocksPerCu) void bc_kernel(const tb_c
     }
 }
 
+// Cap on the batched copy's workgroups set by tb_batched_set_max_workgroups
+// (0: none).  Process-wide; read at each launch.
+static std::atomic<uint32_t> g_bc_max_wgs{0};
+
+void set_batched_max_workgroups(uint32_t max_wgs) { g_bc_max_wgs.store(max_wgs, std::memory_order_relaxed); }
+
+// A grid of g workgroups, capped, as a multiple of 8 (workgroups are dealt to
+// the 8 XCDs in turn), at least 8.
+static int capped_grid(uint64_t g) {
+    const uint32_t cap = g_bc_max_wgs.load(std::memory_order_relaxed);
+    if (cap != 0 && g > cap)
+        g = cap & ~7u;
+    if (g < 8)
+        g = 8;
+    return (int)((g + 7) & ~(uint64_t)7);
+}
+
 int batched_grid(uint32_t ncopies, int cu_count) {
     const uint64_t cus = (uint64_t)(cu_count > 0 ? cu_count : 1);
     uint64_t g = ((uint64_t)ncopies + kBcDescPerWave * 4 - 1) / (kBcDescPerWave * 4);
@@ -707,8 +726,7 @@ int batched_grid(uint32_t ncopies, int cu_count) {
         g = cus * kBcBlocksPerCu;
     if (g > cus * kBcMaxGridPerCu)
         g = cus * kBcMaxGridPerCu;
-    // a multiple of 8 (workgroups are dealt to the 8 XCDs in turn)
-    return (int)((g + 7) & ~(uint64_t)7);
+    return capped_grid(g);
 }
 
 uint32_t batched_scanners(uint32_t ncopies, int grid) {
@@ -747,8 +765,7 @@ hipError_t launch_batched_copy_short(const tb_copy_desc *desc, uint32_t n, BcScr
     uint64_t g = ((uint64_t)n + kBcDescPerWave * 4 - 1) / (kBcDescPerWave * 4);
     if (g > cus * kBcMaxGridPerCu)
         g = cus * kBcMaxGridPerCu;
-    const int grid = (int)((g + 7) & ~(uint64_t)7);
-    return launch_bc(grid, s, done_event, desc, n, scratch, epoch, 0u, 0u, 0u, 0u);
+    return launch_bc(capped_grid(g), s, done_event, desc, n, scratch, epoch, 0u, 0u, 0u, 0u);
 }
 
 // ============================================================================

@@ -218,6 +218,18 @@ enum { TB_BC_NORMAL = 0, TB_BC_NO_WAIT = 1, TB_BC_NO_PIECES = 2 };
 int tb_batched_set_mode(int32_t mode);
 
 /*
+ * Compute-unit budget of the batched copy (Mooncake RFC #5041, Design of
+ * #5040, "Interference with compute", and open question 4 on CU controls):
+ * every later batched-copy launch, through tb_batched_copy or a ring, uses at
+ * most max_workgroups workgroups of 256 threads (rounded down to a multiple
+ * of 8, at least 8); 0 removes the cap (the default).  Fewer workgroups leave
+ * compute units to concurrent kernels; each wave then copies more
+ * descriptors.  The bytes written do not depend on the cap.  Process-wide.
+ * Always TB_OK.
+ */
+int tb_batched_set_max_workgroups(uint32_t max_workgroups);
+
+/*
  * Descriptor-slot ring (Mooncake RFC #5041, Design of #5040, "Descriptor
  * slots" and "Host trims"): batched copies whose descriptors the caller holds
  * in HOST memory, submitted without blocking and polled for completion.

@@ -358,3 +358,35 @@ def test_threads_on_their_own_streams():
         exp = np.full(b.pool_bytes, wl.POOL_FILL, dtype=np.uint8)
         oracle.ref_batch(exp, b.payload, b.desc)
         assert oracle.first_mismatch(pool.cpu().numpy(), exp) == -1
+
+
+@pytest.mark.parametrize("cap", [8, 64, 1000])
+def test_workgroup_cap_gives_identical_bytes(cap):
+    """tb_batched_set_max_workgroups: the same bytes with the grid capped at
+    8, 64 and 1,000 workgroups (each wave then owns many descriptors, and with
+    8 every workgroup is also a scanner), through tb_batched_copy and a ring."""
+    torch = require_gpu()
+    import copy_reduce_amd as tb
+    from copy_reduce_amd.torch_api import DescRing
+    b = wl.batch_c5(seed=60 + cap, pool_bytes=128 << 20, n_block=2500, n_index=800, n_mla=2)
+    note(f"batched copy, grid capped at {cap} workgroups")
+    tb.tb_batched_set_max_workgroups(cap)
+    try:
+        assert tb.tb_launch_info(0, 1, b.ncopies)["batched_blocks"] <= max(8, cap)
+        assert _run_batch(torch, b, launches=2) == -1
+        src = torch.from_numpy(b.payload).cuda()
+        pool = torch.full((b.pool_bytes,), wl.POOL_FILL, dtype=torch.uint8, device="cuda")
+        host = b.desc.astype(np.uint64).copy()
+        host[:, 0] += np.uint64(int(src.data_ptr()))
+        host[:, 1] += np.uint64(int(pool.data_ptr()))
+        torch.cuda.synchronize()
+        with DescRing(nslots=4, slot_descs=1024) as ring:
+            t = 0
+            for a in range(0, b.ncopies, 1000):
+                t = ring.submit(host[a:a + 1000])
+            ring.wait(t)
+    finally:
+        tb.tb_batched_set_max_workgroups(0)
+    exp = np.full(b.pool_bytes, wl.POOL_FILL, dtype=np.uint8)
+    oracle.ref_batch(exp, b.payload, b.desc)
+    assert oracle.first_mismatch(pool.cpu().numpy(), exp) == -1

@@ -177,6 +177,11 @@ def test_timing_hook_needs_no_device():
     assert _st("tb_time_next_launch", None, None) == tb.TB_OK        # cleared again
 
 
+def test_workgroup_cap_needs_no_device():
+    for cap in (0, 1, 8, 4096, 2**32 - 1, 0):                        # ends with the default
+        assert _st("tb_batched_set_max_workgroups", cap) == tb.TB_OK
+
+
 def test_batched_mode_hook_checks():
     for bad in (-1, 3, 1 << 20):
         assert _st("tb_batched_set_mode", bad) == tb.TB_ERR_INVALID
