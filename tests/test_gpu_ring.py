@@ -235,3 +235,36 @@ def test_ring_and_plain_calls_interleave_on_one_stream(direct):
         ring.wait(t)
         s.synchronize()
     assert dev.first_mismatch() == -1
+
+
+def test_two_rings_from_two_threads():
+    """Each host thread drives its own ring on its own stream (a ring is used
+    by one thread at a time; two rings are independent)."""
+    import threading
+    torch = require_gpu()
+    from copy_reduce_amd.torch_api import DescRing
+    devs = [_Dev(torch, wl.batch_c5(seed=70 + t, pool_bytes=64 << 20, n_block=600, n_index=200, n_mla=1))
+            for t in range(2)]
+    streams = [torch.cuda.Stream() for _ in devs]
+    note("two rings, two threads")
+    errors = []
+
+    def work(dev, s, direct):
+        try:
+            with DescRing(nslots=4, slot_descs=128, direct=direct, stream=s) as ring:
+                t = 0
+                for a in range(0, dev.batch.ncopies, 100):
+                    t = ring.submit(dev.host_desc[a:a + 100])
+                ring.wait(t)
+        except Exception as e:  # reported below, in the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=work, args=(d, s, k == 1)) for k, (d, s) in enumerate(zip(devs, streams))]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for dev in devs:
+        assert dev.first_mismatch() == -1
