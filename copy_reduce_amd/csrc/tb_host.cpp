@@ -6,7 +6,9 @@
 #include <string.h>
 
 #include <map>
+#include <memory>
 #include <mutex>
+#include <new>
 #include <string>
 #include <utility>
 
@@ -77,17 +79,19 @@ int device_info(DeviceInfo *out) {
 }
 
 // Batched-copy scratch, one per (device, stream), zeroed once at allocation,
-// with the epoch of the last launch made on it (launches on one stream are
-// ordered, which the kernel's reuse of the scratch relies on).
+// with the epoch of the last launch made on it.  Launches on one scratch must
+// reach their stream in epoch order (each clears what the next one uses), so
+// the epoch is taken and the launch enqueued under the scratch's own lock:
+// threads sharing a stream (the legacy default stream, say) stay in order.
 struct Scratch {
     void *mem = nullptr;
     uint64_t epoch = 0;
+    std::mutex launch_mu;
 };
-std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
+std::map<std::pair<int, hipStream_t>, std::unique_ptr<Scratch>> g_scratch;
 
-// The scratch for `stream` on the current device, and the epoch of the launch
-// about to be made on it (from 1; 64 bits never wrap in practice).
-int scratch_for(hipStream_t stream, tbk::BcScratch **out, uint64_t *epoch) {
+// The scratch for `stream` on the current device, created on first use.
+int scratch_for(hipStream_t stream, Scratch **out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
@@ -96,10 +100,7 @@ int scratch_for(hipStream_t stream, tbk::BcScratch **out, uint64_t *epoch) {
     auto key = std::make_pair(dev, stream);
     auto it = g_scratch.find(key);
     if (it != g_scratch.end()) {
-        Scratch &sc = it->second;
-        sc.epoch += 1;
-        *out = static_cast<tbk::BcScratch *>(sc.mem);
-        *epoch = sc.epoch;
+        *out = it->second.get();
         return TB_OK;
     }
     void *p = nullptr;
@@ -115,12 +116,14 @@ int scratch_for(hipStream_t stream, tbk::BcScratch **out, uint64_t *epoch) {
         (void)hipFree(p);
         return hip_fail(e, "hipMemset(batched-copy scratch)");
     }
-    Scratch sc;
-    sc.mem = p;
-    sc.epoch = 1;
-    g_scratch[key] = sc;
-    *out = static_cast<tbk::BcScratch *>(p);
-    *epoch = 1;
+    std::unique_ptr<Scratch> sc(new (std::nothrow) Scratch);
+    if (!sc) {
+        (void)hipFree(p);
+        return TB_ERR_NOMEM;
+    }
+    sc->mem = p;
+    *out = sc.get();
+    g_scratch[key] = std::move(sc);
     return TB_OK;
 }
 
@@ -303,18 +306,20 @@ int tb_batched_copy(const tb_copy_desc *desc_dev, uint32_t ncopies, void *stream
     int rc = device_info(&info);
     if (rc != TB_OK)
         return rc;
-    tbk::BcScratch *scratch = nullptr;
-    uint64_t epoch = 0;
-    rc = scratch_for(s, &scratch, &epoch);
+    Scratch *sc = nullptr;
+    rc = scratch_for(s, &sc);
     if (rc != TB_OK)
         return rc;
     const int mode = g_batched_mode.load(std::memory_order_relaxed);
     const uint64_t wait_ticks =
         mode == TB_BC_NORMAL ? (uint64_t)tbk::kBcSealWaitUs * info.wall_clock_khz / 1000u : 0u;
-    hipError_t e = tbk::launch_batched_copy(desc_dev, ncopies, scratch, epoch, info.cu_count, wait_ticks,
-                                            mode == TB_BC_NO_PIECES, s);
+    std::lock_guard<std::mutex> lk(sc->launch_mu);
+    const uint64_t epoch = sc->epoch + 1;    // from 1; 64 bits never wrap in practice
+    hipError_t e = tbk::launch_batched_copy(desc_dev, ncopies, static_cast<tbk::BcScratch *>(sc->mem), epoch,
+                                            info.cu_count, wait_ticks, mode == TB_BC_NO_PIECES, s);
     if (e != hipSuccess)
-        return hip_fail(e, "batched-copy launch");
+        return hip_fail(e, "batched-copy launch");   // the epoch is not used up
+    sc->epoch = epoch;
     return TB_OK;
 }
 
@@ -398,7 +403,7 @@ int tb_shutdown(void) {
             (void)hipSetDevice(current);
             return hip_fail(e, "hipDeviceSynchronize");
         }
-        (void)hipFree(kv.second.mem);
+        (void)hipFree(kv.second->mem);
     }
     g_scratch.clear();
     e = hipSetDevice(current);

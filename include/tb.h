@@ -190,6 +190,8 @@ int tb_reduce_copy_ex(float *dst, const float *const *srcs, int32_t nsrc,
  * previous launch on its scratch having finished).  The scratch is found by
  * the stream's handle: synchronise a stream before destroying it if a new
  * stream could be created with the same handle while its copy still runs.
+ * Several host threads may call this on one stream: launches are numbered and
+ * enqueued under the scratch's lock, so they reach the stream in order.
  * Not for HIP graph capture: each launch is numbered on its scratch when it
  * is enqueued, and a replayed capture would repeat the number, so a call on a
  * capturing stream is refused (the reduce-copy has no such state and may be
@@ -325,7 +327,8 @@ int tb_launch_info(uint64_t nfloats, int32_t nsrc, uint32_t ncopies, int32_t *cu
                    int32_t *reduce_blocks, int32_t *batched_blocks);
 
 /* Free the library's scratch and gate memory (waits for the device first).
- * Safe to call more than once; later calls re-allocate lazily. */
+ * Safe to call more than once; later calls re-allocate lazily.  Must not run
+ * concurrently with other calls of the library. */
 int tb_shutdown(void);
 
 #ifdef __cplusplus

@@ -390,3 +390,46 @@ def test_workgroup_cap_gives_identical_bytes(cap):
     exp = np.full(b.pool_bytes, wl.POOL_FILL, dtype=np.uint8)
     oracle.ref_batch(exp, b.payload, b.desc)
     assert oracle.first_mismatch(pool.cpu().numpy(), exp) == -1
+
+
+def test_threads_sharing_one_stream():
+    """Four host threads call tb_batched_copy on the same (default) stream at
+    once: each launch is numbered on the stream's scratch and enqueued under
+    one lock, so the launches reach the stream in the order of their numbers."""
+    import threading
+    torch = require_gpu()
+    import copy_reduce_amd as tb
+    from copy_reduce_amd.torch_api import make_desc
+    jobs = []
+    for t in range(4):
+        b = wl.batch_c5(seed=80 + t, pool_bytes=64 << 20, n_block=300, n_index=100, n_mla=1)
+        src = torch.from_numpy(b.payload).cuda()
+        pool = torch.full((b.pool_bytes,), wl.POOL_FILL, dtype=torch.uint8, device="cuda")
+        desc = make_desc(b.desc, int(src.data_ptr()), int(pool.data_ptr()))
+        jobs.append((b, src, pool, desc))
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    note("batched copy from 4 threads on one stream")
+    errors = []
+    start = threading.Barrier(4)
+
+    def work(job):
+        b, _, _, desc = job
+        try:
+            start.wait()
+            for _ in range(25):
+                tb.tb_batched_copy(int(desc.data_ptr()), b.ncopies, stream.cuda_stream)
+        except Exception as e:  # reported below, in the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=work, args=(j,)) for j in jobs]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for b, _, pool, _ in jobs:
+        exp = np.full(b.pool_bytes, wl.POOL_FILL, dtype=np.uint8)
+        oracle.ref_batch(exp, b.payload, b.desc)
+        assert oracle.first_mismatch(pool.cpu().numpy(), exp) == -1
