@@ -14,8 +14,8 @@
  *   - Calls return a tb_status and never throw; the library prints nothing.
  *   - "device pointer" means memory of the current HIP device (hipMalloc or a
  *     torch CUDA tensor); "host pointer" means ordinary process memory.
- *   - `stream` is a hipStream_t passed as void*; NULL is the legacy default
- *     stream.  GPU work is only enqueued: no call below synchronises unless it
+ *   - `stream` is a hipStream_t of the current device passed as void*; NULL
+ *     is the legacy default stream.  GPU work is only enqueued: no call below synchronises unless it
  *     says so, and the library never touches a stream it was not given.
  *   - The caller owns every buffer it passes.  The library owns only the
  *     batched-copy scratch and the spin-gate flag (freed by tb_shutdown) and
