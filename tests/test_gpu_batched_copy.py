@@ -433,3 +433,55 @@ def test_threads_sharing_one_stream():
         exp = np.full(b.pool_bytes, wl.POOL_FILL, dtype=np.uint8)
         oracle.ref_batch(exp, b.payload, b.desc)
         assert oracle.first_mismatch(pool.cpu().numpy(), exp) == -1
+
+
+def _random_mixed_batch(seed):
+    """A seeded batch mixing empty, tiny, unaligned, page-sized and long copies
+    (some longer than the split size), destinations disjoint with random gaps."""
+    rng = np.random.default_rng(9000 + seed)
+    n = int(rng.choice([1, 2, 63, 64, 65, 500, 1023, 1024, 1025, 3000, 9000]))
+    kind = rng.integers(0, 6, size=n)
+    sizes = np.where(kind == 0, 0,
+             np.where(kind == 1, rng.integers(1, 64, size=n),
+             np.where(kind == 2, rng.integers(64, 4096, size=n),
+             np.where(kind == 3, 64 * rng.integers(1, 257, size=n),
+             np.where(kind == 4, rng.integers(60 * KiB, 70 * KiB, size=n),
+                      rng.integers(64 * KiB, 2 * MiB, size=n)))))).astype(np.int64)
+    if n > 100:                      # keep the total modest: long copies only in a few places
+        longs = np.flatnonzero(sizes > 64 * KiB)
+        sizes[longs[8:]] = rng.integers(1, 2048, size=max(0, longs.size - 8))
+    align = int(rng.choice([1, 4, 16]))
+    src_off, dst_off = np.zeros(n, np.int64), np.zeros(n, np.int64)
+    ps = int(rng.integers(0, 16))
+    for i in range(n):
+        ps = (ps + align - 1) // align * align
+        src_off[i] = ps
+        ps += int(sizes[i]) + int(rng.integers(0, 32))
+    order = rng.permutation(n)
+    pd = int(rng.integers(0, 16))
+    for i in order:
+        pd = (pd + align - 1) // align * align
+        dst_off[i] = pd
+        pd += int(sizes[i]) + int(rng.integers(0, 32))
+    desc = np.stack([src_off, dst_off, sizes], axis=1).astype(np.uint64)
+    return wl.Batch(f"mixed{seed}", desc, ps + 64, pd + 64, seed, payload=wl.random_payload(rng, ps + 64))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_seeded_mixed_batches_under_random_settings(seed):
+    """24 seeded batches of every kind of copy, each under a seeded choice of
+    recovery mode and workgroup cap, launched twice in a row on one stream."""
+    torch = require_gpu()
+    import copy_reduce_amd as tb
+    rng = np.random.default_rng(seed)
+    b = _random_mixed_batch(seed)
+    mode = [tb.TB_BC_NORMAL, tb.TB_BC_NORMAL, tb.TB_BC_NO_WAIT, tb.TB_BC_NO_PIECES][seed % 4]
+    cap = int(rng.choice([0, 0, 8, 64, 512]))
+    note(f"batched mixed seed={seed} n={b.ncopies} bytes={b.total_bytes} mode={mode} cap={cap}")
+    tb.tb_batched_set_mode(mode)
+    tb.tb_batched_set_max_workgroups(cap)
+    try:
+        assert _run_batch(torch, b, src_shift=seed % 7, dst_shift=(seed * 5) % 9, launches=2) == -1
+    finally:
+        tb.tb_batched_set_mode(tb.TB_BC_NORMAL)
+        tb.tb_batched_set_max_workgroups(0)
