@@ -123,6 +123,26 @@ def run_launch_events(torch, tb, stream, launches):
     return [st[j].elapsed_time(sp[j]) for j in range(len(launches))], st[0].elapsed_time(sp[-1])
 
 
+def reduce_copy_mall_flushed(torch, tb, stream, launches):
+    """Each launch after an untimed 1 GiB streaming copy (which evicts the
+    256 MB memory-side cache), timed by its own launch events: per-launch ms."""
+    fa = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
+    fb = torch.empty_like(fa)
+    out = []
+    for fn in launches:
+        tb.tb_reduce_copy(int(fb.data_ptr()), [int(fa.data_ptr())], fa.numel(), stream.cuda_stream)
+        st, sp = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st.record(stream)
+        sp.record(stream)                # a first record creates the events
+        tb.tb_time_next_launch(st.cuda_event, sp.cuda_event)
+        fn()
+        torch.cuda.synchronize()
+        out.append(st.elapsed_time(sp))
+    del fa, fb
+    torch.cuda.empty_cache()
+    return out
+
+
 def device_record(torch, tb):
     """Name, CU count and the partition modes the measurement ran under (the
     cache behaviour rotation guards against depends on them)."""
@@ -222,6 +242,7 @@ def main_line(args, torch, tb, wl):
     total_ms, wall = run_whole(torch, tb, stream, launches)
     ms, total_ms_launch_events = run_launch_events(torch, tb, stream, launches)
     rc_ms, bc_ms = ms[0::2], ms[1::2]
+    rc_flushed_ms = reduce_copy_mall_flushed(torch, tb, stream, [rc(i) for i in range(args.steps)])
 
     rc_bytes, bc_bytes = w.algorithmic_bytes, batch.algorithmic_bytes
     step_bytes = rc_bytes + bc_bytes
@@ -260,7 +281,13 @@ def main_line(args, torch, tb, wl):
         "parts": {
             "reduce_copy": {"ms_mean": round(rc_mean, 5), "ms_min": round(min(rc_ms), 5),
                             "ms_max": round(max(rc_ms), 5), "gbps": round(rc_gbps, 1),
-                            "frac_of_peak": round(rc_gbps / HBM_PEAK_GBPS, 4)},
+                            "frac_of_peak": round(rc_gbps / HBM_PEAK_GBPS, 4),
+                            "mall_flushed": {
+                                "note": "each launch preceded by an untimed 1 GiB copy that evicts the 256 MB "
+                                        "memory-side cache; not the pages' method, the rate without cache help",
+                                "ms_mean": round(statistics.mean(rc_flushed_ms), 5),
+                                "frac_of_peak": round(rc_bytes / (statistics.mean(rc_flushed_ms) * 1e-3) / 1e9
+                                                      / HBM_PEAK_GBPS, 4)}},
             "batched_copy": {"ms_mean": round(bc_mean, 5), "ms_min": round(min(bc_ms), 5),
                              "ms_max": round(max(bc_ms), 5), "gbps": round(bc_gbps, 1),
                              "frac_of_peak": round(bc_gbps / HBM_PEAK_GBPS, 4),
