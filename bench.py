@@ -1077,7 +1077,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): "
-              "this build measures the single-GPU hot path; see DESIGN.md for how it would shard.",
+              "the transfer path measured here runs on one GPU's HBM (sharding across GPUs is designed, not built).",
               file=sys.stderr, flush=True)
         sys.exit(2)
     if args.steps < 1 or args.warmup < 0:
