@@ -120,3 +120,49 @@ def test_batched_copy_millions_of_descriptors():
     exp = np.full(pool_bytes, wl.POOL_FILL, dtype=np.uint8)
     oracle.ref_batch(exp, batch.payload, desc)
     assert oracle.first_mismatch(pool.cpu().numpy(), exp) == -1
+
+
+def test_batched_copy_of_one_copy_above_4GiB():
+    """One descriptor of 4 GiB + 4,109 bytes (its ends 7 bytes past 16-byte
+    boundaries on both sides, so a byte head, a vector body and a byte tail)
+    among 300 small copies: the long copy is cut into more than half a million
+    pieces.  Compared on the device: every destination equals its source, and
+    the guard bytes around the pool are untouched."""
+    torch = require_gpu()
+    import copy_reduce_amd as tb
+    from copy_reduce_amd.torch_api import make_desc
+    big = (4 << 30) + 4109
+    note(f"max size: batched copy with one {big}-byte copy and 300 small ones")
+    rng = np.random.default_rng(31)
+    small = rng.integers(1, 3000, size=300).astype(np.int64)
+    n = 301
+    sizes = np.concatenate([[big], small])
+    src_off = np.zeros(n, np.int64)
+    dst_off = np.zeros(n, np.int64)
+    ps, pd = 7, 23                                     # both 7 mod 16
+    for i in range(n):
+        src_off[i], dst_off[i] = ps, pd
+        ps += int(sizes[i]) + 16 + int(rng.integers(0, 16))
+        pd += int(sizes[i]) + 16 + int(rng.integers(0, 16))
+    perm = rng.permutation(n)
+    desc = np.stack([src_off, dst_off, sizes], axis=1).astype(np.uint64)[perm]
+    src = DevBuf(torch, ps - ps % 4, offset=0)
+    _fill_pattern(torch, src, 3)
+    assert src.nbytes >= int((src_off + sizes).max())
+    dst = DevBuf(torch, pd, offset=0, fill=0x11)
+    d = make_desc(desc, src.ptr, dst.ptr)
+    torch.cuda.synchronize()
+    tb.tb_batched_copy(int(d.data_ptr()), n, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    sb, db = _body(src), _body(dst)
+    for s_, d_, b_ in desc.astype(np.int64):
+        assert torch.equal(db[d_:d_ + b_], sb[s_:s_ + b_]), (s_, d_, b_)
+    # bytes between destinations keep the fill (contiguous slices only: no
+    # advanced indexing on a tensor this large)
+    pos = 0
+    for _, d_, b_ in sorted(desc.astype(np.int64).tolist(), key=lambda r: r[1]):
+        if d_ > pos:
+            assert bool((db[pos:d_] == 0x11).all()), (pos, d_)
+        pos = d_ + b_
+    assert bool((db[pos:] == 0x11).all())
+    assert _guards_on_device(dst)
