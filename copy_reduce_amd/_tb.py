@@ -229,9 +229,15 @@ def tb_ring_create(nslots: int, slot_descs: int, flags: int, stream: int) -> int
 
 
 def tb_ring_submit(ring: int, host_desc_ptr: int, n: int) -> int:
-    """Submit n host descriptors at host_desc_ptr; returns the ticket."""
+    """Submit n host descriptors at host_desc_ptr; returns the ticket.  On a
+    runtime failure the raised TBError carries `ticket`: the ring's last ticket,
+    covering the launches of the request that were enqueued before it."""
     t = _u64()
-    _check("tb_ring_submit", lib.tb_ring_submit(ring, host_desc_ptr, n, ctypes.byref(t)))
+    status = lib.tb_ring_submit(ring, host_desc_ptr, n, ctypes.byref(t))
+    if status != TB_OK:
+        err = TBError("tb_ring_submit", status)
+        err.ticket = t.value if status == TB_ERR_HIP else None
+        raise err
     return t.value
 
 

@@ -394,18 +394,20 @@ int tb_shutdown(void) {
     hipError_t e = hipGetDevice(&current);
     if (e != hipSuccess)
         return hip_fail(e, "hipGetDevice");
-    // every device that holds scratch finishes its work before the scratch goes
-    for (auto &kv : g_scratch) {
-        e = hipSetDevice(kv.first.first);
+    // every device that holds scratch finishes its work before the scratch
+    // goes; an entry leaves the table as its memory is freed, so a failure
+    // part-way leaves only live scratch behind
+    for (auto it = g_scratch.begin(); it != g_scratch.end();) {
+        e = hipSetDevice(it->first.first);
         if (e == hipSuccess)
             e = hipDeviceSynchronize();
         if (e != hipSuccess) {
             (void)hipSetDevice(current);
             return hip_fail(e, "hipDeviceSynchronize");
         }
-        (void)hipFree(kv.second->mem);
+        (void)hipFree(it->second->mem);
+        it = g_scratch.erase(it);
     }
-    g_scratch.clear();
     e = hipSetDevice(current);
     if (e == hipSuccess)
         e = hipDeviceSynchronize();   // the spin gate's device

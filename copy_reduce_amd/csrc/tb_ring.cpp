@@ -170,8 +170,10 @@ int tb_ring_submit(tb_ring *r, const tb_copy_desc *host_desc, uint64_t n, uint64
         const uint64_t t = r->next_ticket;
         const uint32_t k = (uint32_t)((t - 1) % r->nslots);
         int rc = free_slot(r, k);
-        if (rc != TB_OK)
+        if (rc != TB_OK) {
+            *ticket = r->next_ticket - 1;
             return rc;
+        }
         tb_copy_desc *slot = r->host + (size_t)k * r->slot_descs;
         bool any_long = false;
         for (uint32_t i = 0; i < m; i++) {
@@ -183,8 +185,10 @@ int tb_ring_submit(tb_ring *r, const tb_copy_desc *host_desc, uint64_t n, uint64
         if (r->flags == TB_RING_STAGED) {
             tb_copy_desc *dslot = r->dev + (size_t)k * r->slot_descs;
             e = hipMemcpyAsync(dslot, slot, (size_t)m * sizeof(tb_copy_desc), hipMemcpyHostToDevice, r->stream);
-            if (e != hipSuccess)
+            if (e != hipSuccess) {
+                *ticket = r->next_ticket - 1;
                 return tbh::hip_fail(e, "hipMemcpyAsync(ring slot)");
+            }
             read_from = dslot;
         } else {
             read_from = r->host_dev + (size_t)k * r->slot_descs;
@@ -197,8 +201,10 @@ int tb_ring_submit(tb_ring *r, const tb_copy_desc *host_desc, uint64_t n, uint64
                                          mode == TB_BC_NO_PIECES, r->stream, r->event[k]);
         else
             e = tbk::launch_batched_copy_short(read_from, m, r->scratch, t, r->cu_count, r->stream, r->event[k]);
-        if (e != hipSuccess)
+        if (e != hipSuccess) {
+            *ticket = r->next_ticket - 1;
             return tbh::hip_fail(e, "batched-copy launch (ring)");
+        }
         r->held_by[k] = t;
         r->next_ticket = t + 1;
     }

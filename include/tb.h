@@ -272,14 +272,18 @@ int tb_batched_set_max_workgroups(uint32_t max_workgroups);
  *   src and dst and neither range may wrap the address space, and the
  *   ring's stream must not be under graph capture, else TB_ERR_INVALID and
  *   nothing of the request is enqueued.  TB_ERR_HIP if a
- *   wait, copy, launch or event record fails; launches of the request made
- *   before the failure stay enqueued.
+ *   wait, copy or launch fails; launches of the request made before the
+ *   failure stay enqueued, and *ticket then receives the ring's last ticket
+ *   (that of the last launch that was enqueued), so the caller can wait for
+ *   them.
  * tb_ring_poll: *done = 1 if the ticket's launch has finished, else 0.
  *   TB_ERR_INVALID for a ticket not yet handed out; TB_ERR_HIP if the
  *   runtime reports an error for the launch.
- * tb_ring_wait: blocks until the ticket's launch has finished.
+ * tb_ring_wait: blocks until the ticket's launch has finished.  Errors as
+ *   tb_ring_poll.
  * tb_ring_destroy: waits for every launch in flight, then frees the ring.
- *   NULL is a no-op.
+ *   NULL is a no-op.  If the wait fails (the runtime reports a device error)
+ *   the ring is freed all the same and the error is returned.
  */
 typedef struct tb_ring tb_ring;
 enum { TB_RING_STAGED = 0, TB_RING_DIRECT = 1 };
