@@ -17,6 +17,8 @@ Default output is ONE JSON line:
   cpu_baseline the oracle timed on one host core over the same step
 --suite additionally prints one line per configuration (C1-C5, sweep);
 --cpu-suite times the oracle alone on one host core for every configuration.
+The other flags (--baselines, --cache-study, --roofs, --interference, --ring,
+--scatter-study, --calibrate-copy) each run one study instead; see --help.
 """
 import argparse
 import hashlib
@@ -997,7 +999,8 @@ def roofs(args, torch, tb, wl):
     """Streams larger than the 256 MB memory-side cache: through the library,
     a 1 GiB memset (nsrc = 0, writes only), a 16-source reduce of 64 MiB each
     (reads 94% of the bytes) and a 512 MiB copy (half and half); for
-    reference, torch's own fill kernel over 1 GiB."""
+    reference, torch's own fill kernel over 1 GiB.  Then the launch floor:
+    per-launch times of a one-workgroup copy and of a 4 MiB copy."""
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     timer = Timed(torch, tb, stream)
@@ -1033,6 +1036,59 @@ def roofs(args, torch, tb, wl):
     timed("copy: tb_reduce_copy nsrc=1, 512 MiB", lambda: tb.tb_reduce_copy(bp2, [ap], a.numel(), sh),
           1 << 30, 512 * MiB, 512 * MiB)
 
+    # Launch floor: a copy of 64 floats (one workgroup, next to no work) and
+    # C1's 4 MiB copy, 20 launches back to back (one event at each end) and by
+    # each launch's own start and stop events.
+    n1 = 1 << 20
+    for label, nf in (("copy of 256 B (one workgroup)", 64), ("copy of 4 MiB (C1 size)", n1)):
+        fns = [lambda j=j, nf=nf: tb.tb_reduce_copy(bp2, [ap + (j % 8) * 4 * n1], nf, sh) for j in range(20)]
+        for fn in fns[:args.warmup]:
+            fn()
+        loop_ms, _ = run_whole(torch, tb, stream, fns)
+        ev_ms, _ = run_launch_events(torch, tb, stream, fns)
+        print(json.dumps({"launch_floor": {"launch": label, "launches": len(fns),
+                                           "us_per_launch_back_to_back": round(loop_ms * 1e3 / len(fns), 2),
+                                           "us_by_own_launch_events": round(statistics.mean(ev_ms) * 1e3, 2)}}),
+              flush=True)
+
+
+def scatter_study(args, torch, tb, wl):
+    """What C4's destination pattern costs: the same 47,520 copies (sizes,
+    source stream, one launch each) under five destination placements, from
+    C4's random 16 KiB slots to destinations packed like the sources.  Per
+    placement: the kernel's duration by its own launch events and the
+    back-to-back rate, over K_b rotated source replicas."""
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    print(json.dumps({"scatter_device": device_record(torch, tb)}), flush=True)
+    for placement in wl.C4_PLACEMENTS:
+        batch = wl.batch_c4_placed(placement)
+        b = setup_batch(torch, tb, batch, wl.DEFAULT_ROTATE_BYTES)
+
+        def bc(i):
+            d = batch_desc_for(tb, b, i)
+            return lambda: tb.tb_batched_copy(int(d.data_ptr()), batch.ncopies, sh)
+        for i in range(-args.warmup, 0):
+            bc(i)()
+        fns = [bc(i) for i in range(args.steps)]
+        loops, kernels = [], []
+        for _ in range(3):
+            loop_ms, _ = run_whole(torch, tb, stream, fns)
+            ev_ms, _ = run_launch_events(torch, tb, stream, fns)
+            loops.append(loop_ms / len(fns))
+            kernels.append(statistics.mean(ev_ms))
+        km, lm = statistics.median(kernels), statistics.median(loops)
+        nbytes = batch.algorithmic_bytes
+        print(json.dumps({"scatter": {
+            "placement": placement, "copies": batch.ncopies, "payload_bytes": batch.total_bytes, "kb": b["kb"],
+            "pool_span_bytes": int((batch.desc[:, 1] + batch.desc[:, 2]).max()),
+            "kernel_us": round(km * 1e3, 2), "kernel_frac_of_peak": round(nbytes / (km * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "loop_us_per_launch": round(lm * 1e3, 2),
+            "loop_frac_of_peak": round(nbytes / (lm * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "validated_sample": batch_sample_check(torch, b["pool"], batch, b["src"])}}), flush=True)
+        del b
+        torch.cuda.empty_cache()
+
 
 def calibrate_copy(torch, tb):
     """A plain copy of exactly 268,435,456 bytes read and 268,435,456 written per launch."""
@@ -1067,6 +1123,8 @@ def main():
                     help="only time write-only, read-mostly and copy streams larger than the memory-side cache, then exit")
     ap.add_argument("--cache-study", action="store_true",
                     help="only run the rotation / cold / warm / flushed study over sizes and SRC_ROTATE_BYTES, then exit")
+    ap.add_argument("--scatter-study", action="store_true",
+                    help="only time C4's copies under five destination placements (random slots to packed), then exit")
     ap.add_argument("--only", default="",
                     help="comma-separated suite configurations to run (implies --suite; the bench line is skipped)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -1112,6 +1170,9 @@ def main():
         return
     if args.ring:
         ring_study(args, torch, tb, wl)
+        return
+    if args.scatter_study:
+        scatter_study(args, torch, tb, wl)
         return
     if args.suite or args.only:
         suite(args, torch, tb, wl)

@@ -307,6 +307,34 @@ def test_batch_preconditions_hold_and_are_checked():
         far.check()
 
 
+
+def test_c4_placements_keep_the_copies_and_move_only_destinations():
+    """The destination-placement study's batches: C4's sizes (as a multiset),
+    sources packed in descriptor order, valid disjoint destinations, and the
+    placement each one names."""
+    c4 = wl.batch_c4(with_payload=False)
+    ref_sizes = np.sort(c4.desc[:, 2])
+    for p in wl.C4_PLACEMENTS:
+        b = wl.batch_c4_placed(p).check()
+        d = b.desc.astype(np.int64)
+        assert b.ncopies == c4.ncopies and np.array_equal(np.sort(b.desc[:, 2]), ref_sizes)
+        assert d[0, 0] == 0 and np.all(d[1:, 0] == d[:-1, 0] + d[:-1, 2])      # one source stream
+        assert len(b.payload) == b.src_bytes
+        if p == "random_slots":
+            assert np.array_equal(b.desc, c4.desc)
+        elif p == "random_slots_sorted":
+            assert np.all(np.diff(d[:, 1]) > 0)
+            assert np.array_equal(np.sort(d[:, 1]), np.sort(c4.desc[:, 1].astype(np.int64)))
+        elif p == "consecutive_slots":
+            assert np.array_equal(d[:, 1], np.arange(b.ncopies) * wl.SLOT_BYTES)
+        elif p == "packed":
+            assert np.array_equal(d[:, 1], d[:, 0])
+        else:
+            assert int((d[:, 1] + d[:, 2]).max()) == b.total_bytes              # dense ...
+            assert not np.all(np.diff(d[:, 1]) > 0)                            # ... visited out of order
+    with pytest.raises(ValueError):
+        wl.batch_c4_placed("diagonal")
+
 # --------------------------------------------------------------------------
 # Comparator ("How validation (ValidateAllTransfers) works")
 # --------------------------------------------------------------------------

@@ -228,3 +228,40 @@ def batch_random(seed: int, n: int, max_bytes: int, pool_bytes: int,
     b.payload = random_payload(rng, src_total)
     return b
 
+
+
+C4_PLACEMENTS = ("random_slots", "random_slots_sorted", "consecutive_slots", "packed", "packed_shuffled")
+
+
+def batch_c4_placed(placement: str, seed: int = 4, pool_bytes: int = POOL_BYTES) -> Batch:
+    """C4's copies (the same sizes) under another destination placement, for
+    telling what the destination pattern costs.  Sources are always packed in
+    descriptor order, so the reads stay one stream and only the writes change:
+      random_slots         C4 itself: distinct random 16 KiB slots, in drawing order
+      random_slots_sorted  the same slots, descriptors in increasing destination order
+      consecutive_slots    descriptor k in slot k (every slot used, in order)
+      packed               destinations adjacent in descriptor order, like the sources
+      packed_shuffled      the packed destinations, descriptors in a random order."""
+    base = batch_c4(seed=seed, pool_bytes=pool_bytes, with_payload=True)
+    sizes = base.desc[:, 2].copy()
+    dst = base.desc[:, 1].copy()
+    n = len(sizes)
+    if placement == "random_slots":
+        order = np.arange(n)
+    elif placement == "random_slots_sorted":
+        order = np.argsort(dst, kind="stable")
+    elif placement in ("consecutive_slots", "packed"):
+        order = np.arange(n)
+    elif placement == "packed_shuffled":
+        order = np.random.default_rng(seed + 1000).permutation(n)
+    else:
+        raise ValueError(f"unknown placement {placement!r}")
+    sizes, dst = sizes[order], dst[order]
+    if placement == "consecutive_slots":
+        dst = np.arange(n, dtype=np.uint64) * np.uint64(SLOT_BYTES)
+    elif placement in ("packed", "packed_shuffled"):
+        packed, _ = _pack_sources(base.desc[:, 2])       # adjacent, in C4's drawing order
+        dst = packed[order]
+    src_off, src_total = _pack_sources(sizes)
+    desc = np.stack([src_off, dst, sizes], axis=1).astype(np.uint64)
+    return Batch(f"c4_{placement}", desc, src_total, pool_bytes, seed, payload=base.payload[:src_total])
