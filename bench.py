@@ -127,7 +127,9 @@ def run_launch_events(torch, tb, stream, launches):
 
 def reduce_copy_mall_flushed(torch, tb, stream, launches):
     """Each launch after an untimed 1 GiB streaming copy (which evicts the
-    256 MB memory-side cache), timed by its own launch events: per-launch ms."""
+    256 MB memory-side cache), timed by its own launch events: per-launch ms.
+    The flush is the library's one-source copy, whose device-scope stores
+    allocate in that cache; nontemporal stores would leave it in place."""
     fa = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
     fb = torch.empty_like(fa)
     out = []

@@ -11,7 +11,9 @@ namespace tbk {
 
 // ---- reduce-copy -----------------------------------------------------------
 
-// Workgroup size of the reduce-copy kernels (4 wave64s).
+// Workgroup size of the reduce-copy kernels (4 wave64s): the memset, the
+// scalar path, and the vector path up to three sources (from four sources up
+// the vector path runs one-wave workgroups).
 constexpr int kRcBlock = 256;
 // Grid cap of the reduce-copy (a multiple of 8); below it every tile has its
 // own workgroup.

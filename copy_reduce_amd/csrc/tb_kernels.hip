@@ -46,13 +46,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(uint64_t base, uin
                                              0x00020000);
 }
 
-// float4s per thread per tile.  One tile per workgroup with few loads per
-// thread measured best on MI355X: the dispatcher keeps every CU full and no
-// thread holds many registers.
-template <int N>
-constexpr int rc_unroll() {
-    return N <= 2 ? 1 : (N <= 4 ? 2 : 1);
-}
+// Tile shape of the vector path, by number of sources.  One tile per
+// workgroup.  Measured on MI355X (sources of 64 MiB rotated over 4 slices,
+// median of 3 runs): up to three sources, four-wave workgroups of 1 (N <= 2)
+// or 2 (N = 3) float4s per thread reach 84-94%; from four sources up,
+// one-wave workgroups of 2 float4s per thread per source beat them by 2-7
+// points (N = 4: 84.6% against 82.3%; N = 6: 83.6% against 77.1%; N = 16:
+// 81.3% against 77.1%).  At that register footprint a four-wave workgroup
+// must find four free wave slots on one CU at once; a one-wave workgroup
+// fills any free slot.
+constexpr int rc_block_of(int nsrc) { return nsrc >= 4 ? 64 : kRcBlock; }
+constexpr int rc_unroll_of(int nsrc) { return nsrc <= 2 ? 1 : 2; }
 
 template <int N>
 constexpr bool rc_xcd_map() {
@@ -63,10 +67,16 @@ constexpr bool rc_xcd_map() {
 // kernel measured 73% of peak instead of 92%).  Results are written with
 // device-scope (sc1) stores, through L2 to the memory side.  Measured on
 // MI355X, two sources of 256 MiB: with the destination resident in the 256 MB
-// memory-side cache across launches (a fixed destination, as timed by the
-// pages) sc1 stores reach 88% against 77% for nontemporal ones and 83% for
-// plain ones; with that cache flushed before every launch nontemporal stores
-// lead instead (75% against 70%).
+// memory-side cache (MALL) across launches (a fixed destination, as timed by
+// the pages) sc1 stores reach 88-93% against 77% for nontemporal ones and 83%
+// for plain ones.  Above the MALL's size nontemporal system-scope stores
+// (nt sc0 sc1) gain nothing either: one-source copies of 512 MiB ran at
+// 82-84% with both, and the first launch after preparation 85% with sc1
+// against 82%.  Nontemporal stores and loads also leave lines already in the
+// MALL in place: a 1 GiB copy made of them, run between launches to evict
+// it, left a 256 MiB destination resident (91% against 78% after a copy with
+// sc1 stores).
+constexpr int kRcStorePol = kPolSc1;
 __device__ __forceinline__ f32x4 rc_load(const gf32x4 *p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ float rc_load(const gf32 *p) { return __builtin_nontemporal_load(p); }
 
@@ -100,14 +110,15 @@ __device__ __forceinline__ float rc_sum_scalar(const ReduceArgs &a, uint64_t j) 
 }
 
 // Vector path: every pointer is congruent to dst modulo 16.  Tiles of
-// kRcBlock * U float4s; each thread loads U float4s from every source before
-// the first addition, so N * U 16-byte loads per thread are in flight.
+// BS threads x U float4s; each thread loads U float4s from every source
+// before the first addition, so N * U 16-byte loads per thread are in flight.
 // gridDim.x is a multiple of 8 (see reduce_grid), so the grid-stride step
 // keeps a workgroup on its XCD's share of the tiles.
 template <int N>
-__global__ __launch_bounds__(kRcBlock) void rc_vec_kernel(ReduceArgs a) {
-    constexpr int U = rc_unroll<N>();
-    constexpr uint64_t kTile = (uint64_t)kRcBlock * U;
+__global__ __launch_bounds__(rc_block_of(N)) void rc_vec_kernel(ReduceArgs a) {
+    constexpr int BS = rc_block_of(N);
+    constexpr int U = rc_unroll_of(N);
+    constexpr uint64_t kTile = (uint64_t)BS * U;
     const uint64_t nvec = a.nvec;
     const uint64_t ntiles = (nvec + kTile - 1) / kTile;
     const gf32x4 *src[N];
@@ -128,7 +139,7 @@ __global__ __launch_bounds__(kRcBlock) void rc_vec_kernel(ReduceArgs a) {
             for (int k = 0; k < N; k++)
 #pragma unroll
                 for (int u = 0; u < U; u++)
-                    val[k][u] = rc_load(src[k] + i0 + (uint64_t)u * kRcBlock);
+                    val[k][u] = rc_load(src[k] + i0 + (uint64_t)u * BS);
             const __amdgpu_buffer_rsrc_t out =
                 buffer_over(reinterpret_cast<uint64_t>(a.dst + a.head) + base * 16, (uint32_t)(kTile * 16));
 #pragma unroll
@@ -138,7 +149,7 @@ __global__ __launch_bounds__(kRcBlock) void rc_vec_kernel(ReduceArgs a) {
                 for (int k = 1; k < N; k++)
                     acc = acc + val[k][u];
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), out, threadIdx.x * 16,
-                                                       u * kRcBlock * 16, kPolSc1);
+                                                       u * BS * 16, kRcStorePol);
             }
         } else {
             // the last, partial tile: stores past nvec are dropped by the range check
@@ -146,27 +157,29 @@ __global__ __launch_bounds__(kRcBlock) void rc_vec_kernel(ReduceArgs a) {
                 buffer_over(reinterpret_cast<uint64_t>(a.dst + a.head) + base * 16, (uint32_t)((nvec - base) * 16));
 #pragma unroll
             for (int u = 0; u < U; u++) {
-                const uint64_t i = i0 + (uint64_t)u * kRcBlock;
+                const uint64_t i = i0 + (uint64_t)u * BS;
                 if (i < nvec) {
                     f32x4 acc = rc_load(src[0] + i);
 #pragma unroll
                     for (int k = 1; k < N; k++)
                         acc = acc + rc_load(src[k] + i);
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), out,
-                                                           (threadIdx.x + u * kRcBlock) * 16, 0, kPolSc1);
+                                                           (threadIdx.x + u * BS) * 16, 0, kRcStorePol);
                 }
             }
         }
     }
 
-    // Up to 3 floats before the aligned body and 3 after it.
+    // Up to 3 floats before the aligned body (threads 0-2) and 3 after it
+    // (threads 32-34): every block size here has at least 64 threads.
+    static_assert(BS >= 64, "head and tail threads");
     if (blockIdx.x == 0) {
         gf32 *d = (gf32 *)(a.dst);
         if (threadIdx.x < a.head) {
             const uint64_t j = threadIdx.x;
             d[j] = rc_sum_scalar<N>(a, j);
-        } else if (threadIdx.x >= 64 && threadIdx.x < 64 + a.tail) {
-            const uint64_t j = a.head + 4 * nvec + (threadIdx.x - 64);
+        } else if (threadIdx.x >= 32 && threadIdx.x < 32 + a.tail) {
+            const uint64_t j = a.head + 4 * nvec + (threadIdx.x - 32);
             d[j] = rc_sum_scalar<N>(a, j);
         }
     }
@@ -240,7 +253,7 @@ int reduce_grid(uint64_t nfloats, int nsrc, bool vector_path, int cu_count) {
     if (nsrc == 0)
         per_block = (uint64_t)kRcBlock * 4;
     else if (vector_path)
-        per_block = (uint64_t)kRcBlock * 4 * (nsrc <= 2 ? 1 : (nsrc <= 4 ? 2 : 1));
+        per_block = (uint64_t)rc_block_of(nsrc) * 4 * rc_unroll_of(nsrc);
     else
         per_block = (uint64_t)kRcBlock * 4;
     // one workgroup per tile, capped; the kernels loop when the cap binds
@@ -280,7 +293,7 @@ static hipError_t launch(void (*kernel)(KArgs...), int grid, int block, hipStrea
 template <int N>
 static hipError_t launch_n(const ReduceArgs &a, bool vector_path, int grid, hipStream_t s) {
     if (vector_path)
-        return launch(rc_vec_kernel<N>, grid, kRcBlock, s, nullptr, a);
+        return launch(rc_vec_kernel<N>, grid, rc_block_of(N), s, nullptr, a);
     return launch(rc_scalar_kernel<N>, grid, kRcBlock, s, nullptr, a);
 }
 

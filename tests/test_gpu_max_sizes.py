@@ -1,5 +1,6 @@
 """Buffers above 4 GiB.  The reduce-copy kernels cap their grid at 2^20
-workgroups (4 GiB of 4 KiB tiles) and loop over the tiles beyond it.  The
+workgroups (4 GiB of 4 KiB tiles; 2 GiB of 2 KiB tiles per source from four
+sources up) and loop over the tiles beyond it.  The
 oracle's definitions hold at any size and are checked as such: every byte of a
 memset is the memset byte, a one-source reduce-copy equals its source bitwise
 (both on the device), and a two-source sum equals the oracle's on sampled
@@ -81,6 +82,36 @@ def test_reduce2_above_4GiB_sampled():
         exp = oracle.ref_reduce([fa[lo:hi].cpu().numpy(), fb[lo:hi].cpu().numpy()])
         assert oracle.first_mismatch(got, exp) == -1, f"window at element {lo}"
     assert _guards_on_device(dst)
+
+
+@pytest.mark.parametrize("nsrc,n,offset", [
+    (5, (1 << 29) + 515, 8),       # 2 GiB + 2,060 B per source: one-wave tiles past the grid cap
+    (3, (96 << 20) + 5, 4),        # 384 MiB + 20 B per source: four-wave tiles, above the MALL size
+])
+def test_reduce_multi_source_large_sampled(nsrc, n, offset):
+    torch = require_gpu()
+    import copy_reduce_amd as tb
+    note(f"max size: {nsrc}-source sum n={n} offset {offset}, sampled against the oracle")
+    srcs = [DevBuf(torch, n * 4, offset=offset) for _ in range(nsrc)]
+    for k, buf in enumerate(srcs):
+        i = torch.arange(n, dtype=torch.int64, device="cuda")
+        _body(buf).view(torch.float32).copy_(((i * (40503 + 2 * k) + k) % 65521 - 32760).to(torch.float32) * 0.001)
+        del i
+    dst = DevBuf(torch, n * 4, offset=offset, fill=0x11)
+    tb.tb_reduce_copy(dst.ptr, [b.ptr for b in srcs], n, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(12 + nsrc)
+    starts = [0, n - 4096, (n // 2) & ~1023] + [int(x) for x in rng.integers(0, n - 1024, 48)]
+    fd = _body(dst).view(torch.float32)
+    fs = [_body(b).view(torch.float32) for b in srcs]
+    for lo in starts:
+        hi = min(lo + 4096, n)
+        got = fd[lo:hi].cpu().numpy()
+        exp = oracle.ref_reduce([f[lo:hi].cpu().numpy() for f in fs])
+        assert oracle.first_mismatch(got, exp) == -1, f"window at element {lo}"
+    assert _guards_on_device(dst)
+    del srcs, fs
+    torch.cuda.empty_cache()
 
 
 def test_batched_copy_millions_of_descriptors():
