@@ -56,6 +56,19 @@ def test_reduce_copy_pointer_offsets_n2(offs):
     assert dbuf.guards_intact()
 
 
+@pytest.mark.parametrize("nsrc", list(range(1, 17)))
+@pytest.mark.parametrize("off", [4, 8, 12])
+@pytest.mark.parametrize("n", [5, 1029, 3 * 512 + 7, 64 * 1024 + 9])
+def test_reduce_copy_congruent_offsets_all_n(nsrc, off, n):
+    """Every pointer at the same offset from 16-byte alignment: the vector path
+    with 1-3 head floats and a ragged tail, over several tiles of each shape."""
+    torch = require_gpu()
+    note(f"reduce_copy nsrc={nsrc} n={n} all offsets {off}")
+    got, exp, dbuf, _ = _run(torch, _sources(nsrc, n, seed=nsrc), n, dst_off=off, src_offs=[off] * nsrc)
+    assert oracle.first_mismatch(got, exp) == -1
+    assert dbuf.guards_intact()
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_reduce_copy_pointer_offsets_random(seed):
     torch = require_gpu()
