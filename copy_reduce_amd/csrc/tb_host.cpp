@@ -241,7 +241,6 @@ int tb_reduce_copy_ex(float *dst, const float *const *srcs, int32_t nsrc, uint64
     a.dst = dst;
     a.n = nfloats;
     a.fill = memset_byte * 0x01010101u;
-    bool vector_path = true;
     for (int32_t k = 0; k < nsrc; k++) {
         const float *p = srcs[k];
         if (p == nullptr || !aligned4(p))
@@ -253,8 +252,6 @@ int tb_reduce_copy_ex(float *dst, const float *const *srcs, int32_t nsrc, uint64
         // written by the same thread), never partly overlap one.
         if (s0 != d0 && s0 < d0 + nbytes && d0 < s0 + nbytes)
             return TB_ERR_INVALID;
-        if (((s0 ^ d0) & 15u) != 0)
-            vector_path = false;
         a.src[k] = p;
     }
     // Vector split: floats before dst's first 16-byte boundary, float4 body, rest.
@@ -264,8 +261,15 @@ int tb_reduce_copy_ex(float *dst, const float *const *srcs, int32_t nsrc, uint64
     a.head = (uint32_t)head;
     a.nvec = (nfloats - head) / 4;
     a.tail = (uint32_t)((nfloats - head) % 4);
-    if (nsrc == 0)
-        vector_path = true;
+    // Each source's offset from 16-byte alignment at the element that lines
+    // up with dst's first aligned one; all zero takes the plain vector path.
+    bool vector_path = true;
+    for (int32_t k = 0; k < nsrc; k++) {
+        const uintptr_t body = reinterpret_cast<uintptr_t>(a.src[k]) + 4u * head;
+        a.shift[k] = (uint8_t)((body & 15u) / 4u);
+        if (a.shift[k] != 0)
+            vector_path = false;
+    }
 
     DeviceInfo info;
     int rc = device_info(&info);

@@ -11,9 +11,9 @@ namespace tbk {
 
 // ---- reduce-copy -----------------------------------------------------------
 
-// Workgroup size of the reduce-copy kernels (4 wave64s): the memset, the
-// scalar path, and the vector path up to three sources (from four sources up
-// the vector path runs one-wave workgroups).
+// Workgroup size of the reduce-copy kernels (4 wave64s): the memset, and the
+// vector paths up to three sources (from four sources up they run one-wave
+// workgroups).
 constexpr int kRcBlock = 256;
 // Grid cap of the reduce-copy (a multiple of 8); below it every tile has its
 // own workgroup.
@@ -23,19 +23,23 @@ struct ReduceArgs {
     float *dst;
     const float *src[TB_MAX_SRCS];
     uint64_t n;          // floats
-    // Vector split (fast path only): `head` floats before the first 16-byte
-    // aligned element of dst, then `nvec` float4s, then `tail` floats.
+    // Vector split: `head` floats before the first 16-byte aligned element of
+    // dst, then `nvec` float4s, then `tail` floats.
     uint64_t nvec;
     uint32_t head;
     uint32_t tail;
     uint32_t fill;       // 32-bit memset pattern for nsrc == 0
+    // Per source, (address of its element `head`) mod 16, in floats: 0 when
+    // the source agrees with dst modulo 16.
+    uint8_t shift[TB_MAX_SRCS];
 };
 
 // Workgroups the reduce-copy kernel is launched with.
 int reduce_grid(uint64_t nfloats, int nsrc, bool vector_path, int cu_count);
 
-// Enqueue the reduce-copy for nsrc sources.  vector_path: every pointer shares
-// dst's address modulo 16 (head/nvec/tail filled in by the caller).
+// Enqueue the reduce-copy for nsrc sources (head/nvec/tail/shift filled in by
+// the caller).  vector_path: every source agrees with dst modulo 16 (every
+// shift is 0); otherwise the realigning kernel runs.
 hipError_t launch_reduce_copy(const ReduceArgs &args, int nsrc, bool vector_path,
                               int cu_count, hipStream_t stream);
 

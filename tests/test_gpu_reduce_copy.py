@@ -69,6 +69,21 @@ def test_reduce_copy_congruent_offsets_all_n(nsrc, off, n):
     assert dbuf.guards_intact()
 
 
+@pytest.mark.parametrize("nsrc", list(range(1, 17)))
+@pytest.mark.parametrize("dst_off", [0, 4, 8, 12])
+@pytest.mark.parametrize("n", [7, 2053, 64 * 1024 + 3])
+def test_reduce_copy_mixed_offsets_all_n(nsrc, dst_off, n):
+    """Source k at offset 4(k + 1) mod 16: sources that disagree with dst and
+    with each other modulo 16 (the realigning path; one source in four lines up
+    with dst when dst's offset is a multiple of 4 among them)."""
+    torch = require_gpu()
+    offs = [(4 * (k + 1)) % 16 for k in range(nsrc)]
+    note(f"reduce_copy nsrc={nsrc} n={n} dst offset {dst_off} source offsets {offs}")
+    got, exp, dbuf, _ = _run(torch, _sources(nsrc, n, seed=nsrc + 100), n, dst_off=dst_off, src_offs=offs)
+    assert oracle.first_mismatch(got, exp) == -1
+    assert dbuf.guards_intact()
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_reduce_copy_pointer_offsets_random(seed):
     torch = require_gpu()
@@ -100,15 +115,17 @@ def test_reduce_copy_memset_byte(mb):
     assert oracle.first_mismatch(got, exp) == -1 and dbuf.guards_intact()
 
 
-@pytest.mark.parametrize("nsrc", [1, 2, 3, 16])
-def test_reduce_copy_in_place_alias(nsrc):
-    """dst == src0 exactly: every element is read before it is written."""
+@pytest.mark.parametrize("nsrc,other_off", [(1, 0), (2, 0), (3, 0), (16, 0), (2, 4), (3, 8), (5, 12), (16, 4)])
+def test_reduce_copy_in_place_alias(nsrc, other_off):
+    """dst == src0 exactly: every element is read before it is written.  With
+    the other sources off dst's alignment the realigning path runs, with the
+    aliased source at shift 0."""
     import copy_reduce_amd as tb
     torch = require_gpu()
     n = 300001
-    note(f"reduce_copy in-place nsrc={nsrc} n={n}")
+    note(f"reduce_copy in-place nsrc={nsrc} n={n} other sources at offset {other_off}")
     srcs = _sources(nsrc, n, seed=5)
-    bufs = [DevBuf(torch, n * 4).upload(s) for s in srcs]
+    bufs = [DevBuf(torch, n * 4, offset=0 if k == 0 else other_off).upload(s) for k, s in enumerate(srcs)]
     tb.tb_reduce_copy(bufs[0].ptr, [b.ptr for b in bufs], n, torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert oracle.first_mismatch(bufs[0].download().view(np.float32), oracle.ref_reduce(srcs)) == -1
