@@ -18,7 +18,7 @@ Default output is ONE JSON line:
 --suite additionally prints one line per configuration (C1-C5, sweep);
 --cpu-suite times the oracle alone on one host core for every configuration.
 The other flags (--baselines, --cache-study, --roofs, --interference, --ring,
---scatter-study, --calibrate-copy) each run one study instead; see --help.
+--scatter-study, --misaligned, --calibrate-copy) each run one study instead; see --help.
 """
 import argparse
 import hashlib
@@ -1092,6 +1092,45 @@ def scatter_study(args, torch, tb, wl):
         torch.cuda.empty_cache()
 
 
+def misaligned_study(args, torch, tb, wl):
+    """The reduce-copy when its sources disagree with dst modulo 16 (the
+    realigning path) against aligned sources: 256 MiB per buffer, 1-16
+    sources, every source 0, 4 or 8 bytes past a 16-byte boundary while dst
+    sits on one.  Kernel time from the launches' own events, mean of 10 after
+    3 warmups; the result is checked against torch's own binary32 additions in
+    the same order."""
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    n = 64 << 20
+    print(json.dumps({"misaligned_device": device_record(torch, tb)}), flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(17)
+    for nsrc in (1, 2, 4, 8, 16):
+        srcs = [torch.rand(n + 16, device="cuda", generator=gen) for _ in range(nsrc)]
+        dst = torch.empty(n + 16, device="cuda")
+        dp = int(dst.data_ptr())
+        for off_bytes in (0, 4, 8):
+            k = off_bytes // 4
+            ptrs = [int(x.data_ptr()) + off_bytes for x in srcs]
+            fns = [lambda: tb.tb_reduce_copy(dp, ptrs, n, sh)] * args.steps
+            for _ in range(args.warmup):
+                fns[0]()
+            ms, _ = run_launch_events(torch, tb, stream, fns)
+            m = statistics.mean(ms)
+            ref = srcs[0][k:k + n].clone()
+            for x in srcs[1:]:
+                ref += x[k:k + n]
+            ok = torch.equal(dst[:n], ref)
+            del ref
+            print(json.dumps({"misaligned": {
+                "nsrc": nsrc, "bytes_per_buffer": n * 4, "source_offset_bytes": off_bytes,
+                "path": "vector" if off_bytes == 0 else "realigning",
+                "kernel_us": round(m * 1e3, 2),
+                "frac_of_peak": round((nsrc + 1) * n * 4 / (m * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "validated": ok}}),
+                  flush=True)
+        del srcs, dst
+        torch.cuda.empty_cache()
+
+
 def calibrate_copy(torch, tb):
     """A plain copy of exactly 268,435,456 bytes read and 268,435,456 written per launch."""
     nbytes = 256 << 20
@@ -1127,6 +1166,9 @@ def main():
                     help="only run the rotation / cold / warm / flushed study over sizes and SRC_ROTATE_BYTES, then exit")
     ap.add_argument("--scatter-study", action="store_true",
                     help="only time C4's copies under five destination placements (random slots to packed), then exit")
+    ap.add_argument("--misaligned", action="store_true",
+                    help="only time the reduce-copy with sources 0, 4 or 8 bytes off dst's 16-byte alignment "
+                         "(1-16 sources of 256 MiB), then exit")
     ap.add_argument("--only", default="",
                     help="comma-separated suite configurations to run (implies --suite; the bench line is skipped)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -1175,6 +1217,9 @@ def main():
         return
     if args.scatter_study:
         scatter_study(args, torch, tb, wl)
+        return
+    if args.misaligned:
+        misaligned_study(args, torch, tb, wl)
         return
     if args.suite or args.only:
         suite(args, torch, tb, wl)
