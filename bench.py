@@ -332,9 +332,9 @@ def cpu_baseline(torch, w, batch, dst, pool):
     import workloads as wl
     srcs = [oracle.gen_source(w.nfloats, b, w.fill) for b in range(w.nsrc)]
     image = np.full(batch.pool_bytes, wl.POOL_FILL, dtype=np.uint8)
-    # whole steps, repeated until about 10 s of single-core work (at least 3, at most 200)
+    # whole steps, repeated until about 10 s of single-core work (at least 3, at most 400)
     t_rc, t_bc, exp = [], [], None
-    while len(t_rc) < 3 or (sum(t_rc) + sum(t_bc) < CPU_BUDGET_S and len(t_rc) < 200):
+    while len(t_rc) < 3 or (sum(t_rc) + sum(t_bc) < CPU_BUDGET_S and len(t_rc) < 400):
         t, exp = oracle.time_ref_reduce(srcs)
         t_rc.append(t)
         t_bc.append(oracle.time_ref_batch(image, batch.payload, batch.desc))
