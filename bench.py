@@ -1096,7 +1096,8 @@ def misaligned_study(args, torch, tb, wl):
     """The reduce-copy when its sources disagree with dst modulo 16 (the
     realigning path) against aligned sources: 256 MiB per buffer, 1-16
     sources, every source 0, 4 or 8 bytes past a 16-byte boundary while dst
-    sits on one.  Kernel time from the launches' own events, mean of 10 after
+    sits on one.  Then the batched copy over C4's copies with every source
+    shifted by 0, 1, 2, 4 or 8 bytes.  Kernel time from the launches' own events, mean of 10 after
     3 warmups; the result is checked against torch's own binary32 additions in
     the same order."""
     stream = torch.cuda.current_stream()
@@ -1129,6 +1130,31 @@ def misaligned_study(args, torch, tb, wl):
                   flush=True)
         del srcs, dst
         torch.cuda.empty_cache()
+
+    # the batched copy: C4's copies with every source shifted by 0-8 bytes
+    # (destinations unchanged), so source and destination disagree modulo 16
+    import numpy as np
+    from copy_reduce_amd.torch_api import make_desc
+    batch = wl.batch_c4()
+    src = torch.zeros(batch.src_bytes + 4096, dtype=torch.uint8, device="cuda")
+    src[:batch.src_bytes] = torch.from_numpy(batch.payload).cuda()
+    pool = torch.full((batch.pool_bytes,), wl.POOL_FILL, dtype=torch.uint8, device="cuda")
+    for shift in (0, 1, 2, 4, 8):
+        d = batch.desc.copy()
+        d[:, 0] += np.uint64(shift)
+        desc = make_desc(d, int(src.data_ptr()), int(pool.data_ptr()))
+        fns = [lambda: tb.tb_batched_copy(int(desc.data_ptr()), batch.ncopies, sh)] * args.steps
+        for _ in range(args.warmup):
+            fns[0]()
+        ms, _ = run_launch_events(torch, tb, stream, fns)
+        m = statistics.mean(ms)
+        rng = np.random.default_rng(shift)
+        ok = all(torch.equal(pool[int(d[i, 1]):int(d[i, 1] + d[i, 2])], src[int(d[i, 0]):int(d[i, 0] + d[i, 2])])
+                 for i in rng.integers(0, batch.ncopies, 500))
+        print(json.dumps({"misaligned_batch": {
+            "copies": batch.ncopies, "source_shift_bytes": shift, "kernel_us": round(m * 1e3, 2),
+            "frac_of_peak": round(batch.algorithmic_bytes / (m * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "validated_sample_500": ok}}), flush=True)
 
 
 def calibrate_copy(torch, tb):
@@ -1168,7 +1194,7 @@ def main():
                     help="only time C4's copies under five destination placements (random slots to packed), then exit")
     ap.add_argument("--misaligned", action="store_true",
                     help="only time the reduce-copy with sources 0, 4 or 8 bytes off dst's 16-byte alignment "
-                         "(1-16 sources of 256 MiB), then exit")
+                         "(1-16 sources of 256 MiB) and C4's batched copies with sources shifted 0-8 bytes, then exit")
     ap.add_argument("--only", default="",
                     help="comma-separated suite configurations to run (implies --suite; the bench line is skipped)")
     ap.add_argument("--calibrate-copy", action="store_true",

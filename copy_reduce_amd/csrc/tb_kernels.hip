@@ -453,18 +453,6 @@ struct BufElem<1> {
     }
 };
 template <>
-struct BufElem<4> {
-    typedef uint32_t T;
-    template <int Pol>
-    static __device__ __forceinline__ T load(__amdgpu_buffer_rsrc_t r, int vo, int so) {
-        return __builtin_amdgcn_raw_buffer_load_b32(r, vo, so, Pol);
-    }
-    template <int Pol>
-    static __device__ __forceinline__ void store(T v, __amdgpu_buffer_rsrc_t r, int vo, int so) {
-        __builtin_amdgcn_raw_buffer_store_b32(v, r, vo, so, Pol);
-    }
-};
-template <>
 struct BufElem<16> {
     typedef u32x4 T;
     template <int Pol>
@@ -537,31 +525,114 @@ __device__ __forceinline__ void wave_copy_few_bytes(uint64_t s, uint64_t d, uint
     BufElem<1>::store<kBcStorePol>(BufElem<1>::load<kBcLoadPol>(in, lane, 0), out, lane, 0);
 }
 
-// Copy b bytes from s to d with the whole wave; s, d, b are wave-uniform.
-// 16-byte elements when s and d agree modulo 16 (bytes before dst's first
-// 16-byte boundary and after the last one go one per lane), dwords when they
-// agree modulo 4, single bytes otherwise.  Not inlined: it serves the rare
-// cases, and keeping it out of the kernel body keeps the hot path's register
-// allocation small.
-__device__ __noinline__ void wave_copy_any(uint64_t s, uint64_t d, uint64_t b, int lane) {
-    const uint64_t mis = (s ^ d) & 15;
-    if (mis != 0 && (mis & 3) != 0) {
-        wave_copy_buf<1>(s, d, b, lane);
-        return;
+// The 16 bytes starting `m` bytes into the 32 bytes (x, y), m in 1..15 and
+// wave-uniform: output dword k is bytes 4k + m .. 4k + m + 3.
+__device__ __forceinline__ u32x4 bytes_at(u32x4 x, u32x4 y, uint32_t m) {
+    const uint32_t q = m >> 2, r = m & 3;
+    const uint32_t w0 = q == 0 ? x.x : (q == 1 ? x.y : (q == 2 ? x.z : x.w));
+    const uint32_t w1 = q == 0 ? x.y : (q == 1 ? x.z : (q == 2 ? x.w : y.x));
+    const uint32_t w2 = q == 0 ? x.z : (q == 1 ? x.w : (q == 2 ? y.x : y.y));
+    const uint32_t w3 = q == 0 ? x.w : (q == 1 ? y.x : (q == 2 ? y.y : y.z));
+    const uint32_t w4 = q == 0 ? y.x : (q == 1 ? y.y : (q == 2 ? y.z : y.w));
+    u32x4 o;
+    o.x = __builtin_amdgcn_alignbyte(w1, w0, r);
+    o.y = __builtin_amdgcn_alignbyte(w2, w1, r);
+    o.z = __builtin_amdgcn_alignbyte(w3, w2, r);
+    o.w = __builtin_amdgcn_alignbyte(w4, w3, r);
+    return o;
+}
+
+// Lane i's copy of lane i + 1's x (DPP wave shift left by one lane); lane 63
+// gets `last`.
+__device__ __forceinline__ u32x4 shl1_lane(u32x4 x, u32x4 last) {
+    constexpr int kWaveShl1 = 0x130;
+    u32x4 y;
+    y.x = (uint32_t)__builtin_amdgcn_update_dpp((int)last.x, (int)x.x, kWaveShl1, 0xF, 0xF, false);
+    y.y = (uint32_t)__builtin_amdgcn_update_dpp((int)last.y, (int)x.y, kWaveShl1, 0xF, 0xF, false);
+    y.z = (uint32_t)__builtin_amdgcn_update_dpp((int)last.z, (int)x.z, kWaveShl1, 0xF, 0xF, false);
+    y.w = (uint32_t)__builtin_amdgcn_update_dpp((int)last.w, (int)x.w, kWaveShl1, 0xF, 0xF, false);
+    return y;
+}
+
+// Lane i's copy of lane i + 1's x, and lane 63's of lane 0's (DPP wave
+// rotate left by one lane).
+__device__ __forceinline__ u32x4 rol1_lane(u32x4 x) {
+    constexpr int kWaveRol1 = 0x134;
+    u32x4 y;
+    y.x = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x.x, kWaveRol1, 0xF, 0xF, false);
+    y.y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x.y, kWaveRol1, 0xF, 0xF, false);
+    y.z = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x.z, kWaveRol1, 0xF, 0xF, false);
+    y.w = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x.w, kWaveRol1, 0xF, 0xF, false);
+    return y;
+}
+
+// Slots per step of the realigning copy: 4 KiB steps keep it within the
+// kernel's register budget without spilling.
+constexpr int kBcShiftSlots = 4;
+
+// Copy nblk 16-byte blocks to d (16-byte aligned) from s, which lies m = s mod
+// 16 (1..15) bytes past a 16-byte boundary, with the whole wave.  Source
+// block i of the aligned view A = s - m holds the first 16 - m bytes of
+// destination block i, block i + 1 the rest.  Steps of kBcShiftSlots slots of
+// 64 blocks: each lane loads A's block for its destination block and takes the
+// next one from lane + 1 by DPP; lane 63's next block is lane 0's block of the
+// following slot (rotated in), and only the step's last slot loads it for
+// lane 63.  Block indexes are clamped to the step's last block b0 + nstep
+// (at most nblk, the last block of A that holds a source byte), so every load
+// reads a 16-byte block holding a copied byte; stores are predicated on lying
+// inside the destination.
+__device__ __forceinline__ void wave_copy_shifted(uint64_t s, uint64_t d, uint64_t nblk, int lane) {
+    constexpr int kSlots = kBcShiftSlots;
+    const uint32_t m = (uint32_t)(s & 15);
+    const uint64_t a = s - m;
+    for (uint64_t b0 = 0; b0 < nblk; b0 += (uint64_t)kSlots * 64) {
+        const uint64_t left = nblk - b0;
+        const uint32_t nstep = (uint32_t)(left < (uint64_t)kSlots * 64 ? left : (uint64_t)kSlots * 64);
+        // blocks b0 .. b0 + nstep of A: every one holds a source byte
+        const __amdgpu_buffer_rsrc_t in = buffer_over(a + b0 * 16, (nstep + 1) * 16u);
+        u32x4 x[kSlots];
+#pragma unroll
+        for (int u = 0; u < kSlots; u++) {
+            const uint32_t q = (uint32_t)u * 64 + (uint32_t)lane;
+            x[u] = BufElem<16>::load<kBcLoadPol>(in, (q < nstep ? q : nstep) * 16, 0);
+        }
+        u32x4 z = {0u, 0u, 0u, 0u};
+        if (lane == 63)
+            z = BufElem<16>::load<kBcLoadPol>(in, nstep * 16, 0);   // block b0 + 64 kSlots, clamped
+        const __amdgpu_buffer_rsrc_t out = buffer_over(d + b0 * 16, nstep * 16u);
+#pragma unroll
+        for (int u = 0; u < kSlots; u++) {
+            const u32x4 next = u + 1 < kSlots ? rol1_lane(x[u + 1 < kSlots ? u + 1 : u]) : z;
+            const u32x4 y = shl1_lane(x[u], next);
+            const uint32_t q = (uint32_t)u * 64 + (uint32_t)lane;
+            if (q < nstep)
+                BufElem<16>::store<kBcStorePol>(bytes_at(x[u], y, m), out, q * 16, 0);
+        }
     }
-    const uint64_t g = mis == 0 ? 16 : 4;
-    uint64_t head = (g - (d & (g - 1))) & (g - 1);
+}
+
+// Copy b bytes from s to d with the whole wave; s, d, b are wave-uniform, any
+// alignment.  The bytes before d's first 16-byte boundary and after its last
+// one go one per lane; the 16-byte blocks between are copied directly when s
+// is then aligned too, and realigned in registers otherwise
+// (wave_copy_shifted).  Not inlined: it serves the rare cases, and keeping it
+// out of the kernel body keeps the hot path's register allocation small.
+__device__ __noinline__ void wave_copy_any(uint64_t s, uint64_t d, uint64_t b, int lane) {
+    uint64_t head = (16 - (d & 15)) & 15;
     if (head > b)
         head = b;
     wave_copy_few_bytes(s, d, head, lane);
     s += head;
     d += head;
     b -= head;
-    const uint64_t body = b & ~(g - 1);
-    if (g == 16)
-        wave_copy_buf<16>(s, d, body >> 4, lane);
-    else
-        wave_copy_buf<4>(s, d, body >> 2, lane);
+    const uint64_t nblk = b >> 4;
+    if (nblk != 0) {
+        if ((s & 15) == 0)
+            wave_copy_buf<16>(s, d, nblk, lane);
+        else
+            wave_copy_shifted(s, d, nblk, lane);
+    }
+    const uint64_t body = nblk << 4;
     wave_copy_few_bytes(s + body, d + body, b - body, lane);
 }
 
