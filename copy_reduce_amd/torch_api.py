@@ -81,8 +81,9 @@ def reduce_copy(dst, srcs, nfloats: Optional[int] = None, stream: Optional[torch
     elif nfloats is None:
         raise ValueError("nfloats is required with raw addresses")
     for s in srcs:
-        if isinstance(s, torch.Tensor) and (s.dtype != torch.float32 or not s.is_cuda or s.numel() < nfloats):
-            raise ValueError("sources must be float32 CUDA tensors of at least nfloats elements")
+        if isinstance(s, torch.Tensor) and (s.dtype != torch.float32 or not s.is_cuda or not s.is_contiguous()
+                                            or s.numel() < nfloats):
+            raise ValueError("sources must be contiguous float32 CUDA tensors of at least nfloats elements")
     _tb.tb_reduce_copy(_addr(dst), [_addr(s) for s in srcs], nfloats, stream_handle(stream), memset_byte)
 
 

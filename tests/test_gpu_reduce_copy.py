@@ -131,6 +131,21 @@ def test_reduce_copy_in_place_alias(nsrc, other_off):
     assert oracle.first_mismatch(bufs[0].download().view(np.float32), oracle.ref_reduce(srcs)) == -1
 
 
+def test_torch_api_rejects_strided_tensors():
+    """A strided view would be read as if it were contiguous: the torch layer refuses it."""
+    torch = require_gpu()
+    from copy_reduce_amd.torch_api import reduce_copy
+    a = torch.ones(2048, device="cuda")
+    dst = torch.zeros(1024, device="cuda")
+    with pytest.raises(ValueError):
+        reduce_copy(dst, [a[::2]])
+    with pytest.raises(ValueError):
+        reduce_copy(torch.zeros(2048, device="cuda")[::2], [a[:1024]])
+    reduce_copy(dst, [a[:1024], a[1024:]])
+    torch.cuda.synchronize()
+    assert bool((dst == 2.0).all())
+
+
 def test_reduce_copy_special_values():
     torch = require_gpu()
     n = 4096
