@@ -1002,7 +1002,8 @@ def roofs(args, torch, tb, wl):
     a 1 GiB memset (nsrc = 0, writes only), a 16-source reduce of 64 MiB each
     (reads 94% of the bytes) and a 512 MiB copy (half and half); for
     reference, torch's own fill kernel over 1 GiB.  Then the launch floor:
-    per-launch times of a one-workgroup copy and of a 4 MiB copy."""
+    per-launch times of a one-workgroup copy and of a 4 MiB copy, and the
+    host's cost of one tb_reduce_copy call for 1-16 sources."""
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     timer = Timed(torch, tb, stream)
@@ -1052,6 +1053,27 @@ def roofs(args, torch, tb, wl):
                                            "us_per_launch_back_to_back": round(loop_ms * 1e3 / len(fns), 2),
                                            "us_by_own_launch_events": round(statistics.mean(ev_ms) * 1e3, 2)}}),
               flush=True)
+
+    # Host cost of one call: 200 tb_reduce_copy calls of 64 floats enqueued
+    # while the spin gate holds the stream (so no call waits for the GPU),
+    # timed on the host through this binding (median of 3 rounds).
+    for nsrc in (1, 2, 4, 8, 16):
+        ptrs = [ap + 4096 * k for k in range(nsrc)]
+        per_call = []
+        for _ in range(3):
+            torch.cuda.synchronize()
+            tb.tb_spin_gate_arm(GATE_TIMEOUT_MS, sh)
+            t0 = time.perf_counter()
+            for _ in range(200):
+                tb.tb_reduce_copy(bp2, ptrs, 64, sh)
+            t1 = time.perf_counter()
+            tb.tb_spin_gate_release()
+            torch.cuda.synchronize()
+            if tb.tb_spin_gate_status() != tb.TB_OK:
+                raise RuntimeError("spin gate timed out: the calls were not gated")
+            per_call.append((t1 - t0) / 200)
+        print(json.dumps({"host_enqueue": {"call": f"tb_reduce_copy nsrc={nsrc}, 64 floats", "calls": 200,
+                                           "us_per_call": round(statistics.median(per_call) * 1e6, 2)}}), flush=True)
 
 
 def scatter_study(args, torch, tb, wl):
