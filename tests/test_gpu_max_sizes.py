@@ -1,7 +1,7 @@
 """Buffers above 4 GiB.  The reduce-copy kernels cap their grid at 2^20
 workgroups (4 GiB of 4 KiB tiles; 2 GiB of 2 KiB tiles per source from four
-sources up, 1 GiB of 1 KiB tiles when such sources disagree with dst modulo 16)
-and loop over the tiles beyond it.  The
+sources up; 1 GiB of 1 KiB tiles above eight sources when some source
+disagrees with dst modulo 16) and loop over the tiles beyond it.  The
 oracle's definitions hold at any size and are checked as such: every byte of a
 memset is the memset byte, a one-source reduce-copy equals its source bitwise
 (both on the device), and a two-source sum equals the oracle's on sampled
@@ -88,7 +88,7 @@ def test_reduce2_above_4GiB_sampled():
 @pytest.mark.parametrize("nsrc,n,offset,src_step", [
     (5, (1 << 29) + 515, 8, 0),    # 2 GiB + 2,060 B per source: one-wave tiles past the grid cap
     (3, (96 << 20) + 5, 4, 0),     # 384 MiB + 20 B per source: four-wave tiles, above the MALL size
-    (4, (1 << 28) + 261, 0, 4),    # 1 GiB + 1,044 B, sources 4/8/12/0 B off dst: realigning tiles past the cap
+    (9, (1 << 28) + 261, 0, 4),    # 1 GiB + 1,044 B, sources 4/8/12/0 B off dst: realigning 1 KiB tiles past the cap
 ])
 def test_reduce_multi_source_large_sampled(nsrc, n, offset, src_step):
     torch = require_gpu()
