@@ -35,6 +35,24 @@ def test_header_symbols_exported():
     assert set(declared) <= syms
 
 
+def test_c_consumer_check_builds(tmp_path):
+    """The plain-C program the GPU tests run compiles and links against
+    libtb.so and the HIP runtime (gcc, C11, warnings as errors)."""
+    import importlib.util
+    import shutil
+    spec = importlib.util.spec_from_file_location("_capi_build", os.path.join(ROOT, "tests", "capi", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    if not os.path.exists(os.path.join(ROOT, "copy_reduce_amd", "libtb.so")):
+        pytest.skip("libtb.so not built")
+    here = tmp_path / "capi"
+    here.mkdir()
+    shutil.copy(os.path.join(ROOT, "tests", "capi", "capi_check.c"), here)
+    mod.HERE, mod.OUT = str(here), str(here / "capi_check")
+    out = mod.build()
+    assert os.access(out, os.X_OK)
+
+
 def test_header_compiles_as_plain_c(tmp_path):
     src = tmp_path / "use.c"
     src.write_text('#include "tb.h"\nint main(void){uint64_t k; return tb_num_slices(1,2,&k);}\n')
