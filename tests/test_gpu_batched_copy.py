@@ -118,6 +118,33 @@ def test_large_copies_split_and_queue_reset_across_launches():
         assert _run_batch(torch, batch, launches=2 + rep) == -1
 
 
+@pytest.mark.parametrize("mode", ["TB_BC_NORMAL", "TB_BC_NO_PIECES"])
+def test_long_copies_every_relative_offset(mode):
+    """Copies above the split size at every (source, destination) offset modulo
+    16: pieces that start inside 16-byte blocks, realigned in registers, and
+    (TB_BC_NO_PIECES) the recovery path's whole-copy routine."""
+    import copy_reduce_amd as tb
+    torch = require_gpu()
+    rng = np.random.default_rng(16)
+    size = 200 * KiB + 7
+    slot = 256 * KiB
+    rows = []
+    ps = 0
+    for so in range(16):
+        for do in range(16):
+            k = len(rows)
+            rows.append((ps + so, k * slot + do, size))
+            ps += size + 64
+    desc = np.array(rows, dtype=np.uint64)
+    batch = wl.Batch("long_every_offset", desc, ps + 64, len(rows) * slot, 16, payload=wl.random_payload(rng, ps + 64))
+    tb.tb_batched_set_mode(getattr(tb, mode))
+    try:
+        note(f"batched long copies at all 256 offset pairs, mode {mode}")
+        assert _run_batch(torch, batch) == -1
+    finally:
+        tb.tb_batched_set_mode(tb.TB_BC_NORMAL)
+
+
 def test_queue_overflow_runs_on_owner_waves():
     """More long copies than the queue holds: the overflow ones are copied by
     the scanning wave that found them."""
