@@ -36,6 +36,9 @@ MUTANTS = [
     ("reverse_order",
      "memcpy(dst, srcs[0], (size_t)(n * 4u));\n    for (int k = 2; k <= nsrc; k++) {\n        const float *next = srcs[k - 1];",
      "memcpy(dst, srcs[nsrc - 1], (size_t)(n * 4u));\n    for (int k = 2; k <= nsrc; k++) {\n        const float *next = srcs[nsrc - k];"),
+    ("accumulate_in_double",
+     "memcpy(dst, srcs[0], (size_t)(n * 4u));\n    for (int k = 2; k <= nsrc; k++) {\n        const float *next = srcs[k - 1];\n        for (uint64_t i = 0; i < n; i++)\n            dst[i] = dst[i] + next[i];\n    }",
+     "for (uint64_t i = 0; i < n; i++) {\n        double acc = srcs[0][i];\n        for (int k = 2; k <= nsrc; k++)\n            acc += srcs[k - 1][i];\n        dst[i] = (float)acc;\n    }"),
     ("memset_ignored", "memset(dst, (int)(memset_byte & 0xFFu), (size_t)(n * 4u));", "memset(dst, 0, (size_t)(n * 4u));"),
     ("batch_swapped_offsets", "memcpy(pool + dst_off, src_image + src_off, (size_t)bytes);",
      "memcpy(pool + src_off, src_image + dst_off, (size_t)bytes);"),
