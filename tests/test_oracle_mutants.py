@@ -39,6 +39,7 @@ MUTANTS = [
     ("accumulate_in_double",
      "memcpy(dst, srcs[0], (size_t)(n * 4u));\n    for (int k = 2; k <= nsrc; k++) {\n        const float *next = srcs[k - 1];\n        for (uint64_t i = 0; i < n; i++)\n            dst[i] = dst[i] + next[i];\n    }",
      "for (uint64_t i = 0; i < n; i++) {\n        double acc = srcs[0][i];\n        for (int k = 2; k <= nsrc; k++)\n            acc += srcs[k - 1][i];\n        dst[i] = (float)acc;\n    }"),
+    ("pattern_index_shift", "out[i] = pattern[i % pattern_len];", "out[i] = pattern[(i + 1) % pattern_len];"),
     ("memset_ignored", "memset(dst, (int)(memset_byte & 0xFFu), (size_t)(n * 4u));", "memset(dst, 0, (size_t)(n * 4u));"),
     ("batch_swapped_offsets", "memcpy(pool + dst_off, src_image + src_off, (size_t)bytes);",
      "memcpy(pool + src_off, src_image + dst_off, (size_t)bytes);"),
