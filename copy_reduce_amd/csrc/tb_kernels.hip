@@ -566,9 +566,12 @@ __device__ __forceinline__ u32x4 rol1_lane(u32x4 x) {
     return y;
 }
 
-// Slots per step of the realigning copy: 4 KiB steps keep it within the
-// kernel's register budget without spilling.
-constexpr int kBcShiftSlots = 4;
+// Slots per step of the realigning copy: with 3 KiB steps the routine needs
+// 66 VGPRs, which leaves the kernel, calling it, room to keep its own values
+// in registers (with 4 KiB steps, 72 VGPRs, the kernel spilled one VGPR to
+// scratch around the call in the long-copy piece phase: 1.8 MB of extra HBM
+// writes per launch on a batch with long copies).
+constexpr int kBcShiftSlots = 3;
 
 // Copy nblk 16-byte blocks to d (16-byte aligned) from s, which lies m = s mod
 // 16 (1..15) bytes past a 16-byte boundary, with the whole wave.  Source
