@@ -57,10 +57,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(uint64_t base, uin
 // fills any free slot.
 constexpr int rc_block_of(int nsrc) { return nsrc >= 4 ? 64 : kRcBlock; }
 constexpr int rc_unroll_of(int nsrc) { return nsrc <= 2 ? 1 : 2; }
-// The realigning path holds two float4s per source and unroll step; from
-// four sources up it keeps one step per thread so that sixteen sources stay
-// within 128 VGPRs of loaded data.
-constexpr int rc_shift_unroll_of(int nsrc) { return nsrc > 8 ? 1 : rc_unroll_of(nsrc); }
+// The realigning path gives each wave two contiguous sub-tiles of 64 blocks
+// per source, whatever the source count (see rc_shift_kernel).
+constexpr int rc_shift_unroll_of(int) { return 2; }
 
 template <int N>
 constexpr bool rc_xcd_map() {
@@ -201,15 +200,27 @@ __device__ __forceinline__ f32x4 rc_funnel(u32x4 x, u32x4 y, uint32_t r) {
     return __builtin_bit_cast(f32x4, o);
 }
 
-// Lane i's copy of lane i + 1's x (DPP wave shift left by one lane, a VALU
-// move); lane 63, which has no right neighbour in its wave, keeps `own`.
-__device__ __forceinline__ u32x4 next_lane_block(u32x4 x, u32x4 own) {
+// Lane i's copy of lane i + 1's x (DPP wave shift left by one lane); lane 63
+// gets `last`.
+__device__ __forceinline__ u32x4 shl1_lane(u32x4 x, u32x4 last) {
     constexpr int kWaveShl1 = 0x130;
     u32x4 y;
-    y.x = (uint32_t)__builtin_amdgcn_update_dpp((int)own.x, (int)x.x, kWaveShl1, 0xF, 0xF, false);
-    y.y = (uint32_t)__builtin_amdgcn_update_dpp((int)own.y, (int)x.y, kWaveShl1, 0xF, 0xF, false);
-    y.z = (uint32_t)__builtin_amdgcn_update_dpp((int)own.z, (int)x.z, kWaveShl1, 0xF, 0xF, false);
-    y.w = (uint32_t)__builtin_amdgcn_update_dpp((int)own.w, (int)x.w, kWaveShl1, 0xF, 0xF, false);
+    y.x = (uint32_t)__builtin_amdgcn_update_dpp((int)last.x, (int)x.x, kWaveShl1, 0xF, 0xF, false);
+    y.y = (uint32_t)__builtin_amdgcn_update_dpp((int)last.y, (int)x.y, kWaveShl1, 0xF, 0xF, false);
+    y.z = (uint32_t)__builtin_amdgcn_update_dpp((int)last.z, (int)x.z, kWaveShl1, 0xF, 0xF, false);
+    y.w = (uint32_t)__builtin_amdgcn_update_dpp((int)last.w, (int)x.w, kWaveShl1, 0xF, 0xF, false);
+    return y;
+}
+
+// Lane i's copy of lane i + 1's x, and lane 63's of lane 0's (DPP wave
+// rotate left by one lane).
+__device__ __forceinline__ u32x4 rol1_lane(u32x4 x) {
+    constexpr int kWaveRol1 = 0x134;
+    u32x4 y;
+    y.x = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x.x, kWaveRol1, 0xF, 0xF, false);
+    y.y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x.y, kWaveRol1, 0xF, 0xF, false);
+    y.z = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x.z, kWaveRol1, 0xF, 0xF, false);
+    y.w = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x.w, kWaveRol1, 0xF, 0xF, false);
     return y;
 }
 
@@ -219,16 +230,20 @@ __device__ __forceinline__ u32x4 next_lane_block(u32x4 x, u32x4 own) {
 // floats into the source's aligned 16-byte block i, so a thread needs the
 // source's aligned blocks i and i + 1.  It loads block i (a nontemporal
 // 16-byte load, as on the vector path) and takes block i + 1 from the next
-// lane with a DPP wave shift; only lane 63 loads its block i + 1 itself.  The
-// four floats at the offset are then selected in registers and summed in the
+// lane with a DPP wave shift.  A wave covers two contiguous sub-tiles of 64
+// blocks, so lane 63's block i + 1 in the first is lane 0's block in the
+// second (a DPP wave rotate); only the second's lane 63 loads it.  The four
+// floats at the offset are then selected in registers and summed in the
 // fixed order.  Block indexes are clamped to the last block that holds one
 // of the tile's source elements (the block past the tile's last one when
 // shift[k] > 0), so only whole 16-byte blocks holding a source element are
 // read; a lane past the tile's end re-reads a block and stores nothing.
-// Measured at 256 MiB per buffer, one source 4 or 8 bytes off dst, against
-// the per-float path this replaced: 80% against 74% (one source), 89% against
-// 79% (two), 80% against 78% (four), 77% against 72% (eight), 70% against 66%
-// (sixteen).  Loading block i + 1 as well instead of the DPP shift measured
+// Measured at 256 MiB per buffer, every source 4 or 8 bytes off dst: 93%
+// (one source), 89-90% (two), 79-80% (four), 75-76% (eight), 73% (sixteen).
+// One sub-tile per wave, each lane 63 loading its own block i + 1, measured
+// 81%, 89%, 80-81%, 76-77% and 70%: the single-lane load per wave and source
+// cost one source 12 points.  The per-float path this replaced ran at 74%,
+// 79%, 78%, 72% and 66%; loading block i + 1 as well instead of the DPP shift,
 // 73%, 79% and 59% for one, two and four sources.
 template <int N>
 __global__ __launch_bounds__(rc_block_of(N)) void rc_shift_kernel(ReduceArgs a) {
@@ -245,7 +260,12 @@ __global__ __launch_bounds__(rc_block_of(N)) void rc_shift_kernel(ReduceArgs a) 
             continue;
         const uint64_t base = t * kTile;
         const uint32_t nblk = (uint32_t)(nvec - base < kTile ? nvec - base : kTile);   // dst blocks here
-        u32x4 xs[N][U], ys[N][U];
+        // This wave's U sub-tiles of 64 blocks are contiguous, so lane 63's
+        // block i + 1 in sub-tile u is lane 0's block in sub-tile u + 1; only
+        // the last sub-tile's lane 63 loads it.
+        const uint32_t lane = threadIdx.x & 63u;
+        const uint32_t wbase = (threadIdx.x >> 6) * (uint32_t)(U * 64);
+        u32x4 xs[N][U], zs[N];
 #pragma unroll
         for (int k = 0; k < N; k++) {
             const uint32_t r = a.shift[k];
@@ -254,26 +274,26 @@ __global__ __launch_bounds__(rc_block_of(N)) void rc_shift_kernel(ReduceArgs a) 
             const gu32x4 *in = (const gu32x4 *)first;
 #pragma unroll
             for (int u = 0; u < U; u++) {
-                const uint32_t q = threadIdx.x + (uint32_t)u * BS;
-                const uint32_t qx = q < last ? q : last;
-                const uint32_t qy = q + 1 < last ? q + 1 : last;
-                xs[k][u] = __builtin_nontemporal_load(in + qx);
-                u32x4 z = {0u, 0u, 0u, 0u};
-                if ((threadIdx.x & 63) == 63)
-                    z = __builtin_nontemporal_load(in + qy);
-                ys[k][u] = z;
+                const uint32_t q = wbase + (uint32_t)u * 64u + lane;
+                xs[k][u] = __builtin_nontemporal_load(in + (q < last ? q : last));
             }
+            const uint32_t qz = wbase + (uint32_t)(U * 64);
+            u32x4 z = {0u, 0u, 0u, 0u};
+            if (lane == 63)
+                z = __builtin_nontemporal_load(in + (qz < last ? qz : last));
+            zs[k] = z;
         }
+        u32x4 ys[N][U];
 #pragma unroll
         for (int k = 0; k < N; k++)
 #pragma unroll
             for (int u = 0; u < U; u++)
-                ys[k][u] = next_lane_block(xs[k][u], ys[k][u]);
+                ys[k][u] = shl1_lane(xs[k][u], u + 1 < U ? rol1_lane(xs[k][u + 1 < U ? u + 1 : u]) : zs[k]);
         const __amdgpu_buffer_rsrc_t out =
             buffer_over(reinterpret_cast<uint64_t>(a.dst + a.head) + base * 16, nblk * 16u);
 #pragma unroll
         for (int u = 0; u < U; u++) {
-            const uint32_t q = threadIdx.x + (uint32_t)u * BS;
+            const uint32_t q = wbase + (uint32_t)u * 64u + lane;
             if (q < nblk) {
                 f32x4 acc = rc_funnel(xs[0][u], ys[0][u], a.shift[0]);
 #pragma unroll
@@ -542,29 +562,6 @@ __device__ __forceinline__ u32x4 bytes_at(u32x4 x, u32x4 y, uint32_t m) {
     return o;
 }
 
-// Lane i's copy of lane i + 1's x (DPP wave shift left by one lane); lane 63
-// gets `last`.
-__device__ __forceinline__ u32x4 shl1_lane(u32x4 x, u32x4 last) {
-    constexpr int kWaveShl1 = 0x130;
-    u32x4 y;
-    y.x = (uint32_t)__builtin_amdgcn_update_dpp((int)last.x, (int)x.x, kWaveShl1, 0xF, 0xF, false);
-    y.y = (uint32_t)__builtin_amdgcn_update_dpp((int)last.y, (int)x.y, kWaveShl1, 0xF, 0xF, false);
-    y.z = (uint32_t)__builtin_amdgcn_update_dpp((int)last.z, (int)x.z, kWaveShl1, 0xF, 0xF, false);
-    y.w = (uint32_t)__builtin_amdgcn_update_dpp((int)last.w, (int)x.w, kWaveShl1, 0xF, 0xF, false);
-    return y;
-}
-
-// Lane i's copy of lane i + 1's x, and lane 63's of lane 0's (DPP wave
-// rotate left by one lane).
-__device__ __forceinline__ u32x4 rol1_lane(u32x4 x) {
-    constexpr int kWaveRol1 = 0x134;
-    u32x4 y;
-    y.x = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x.x, kWaveRol1, 0xF, 0xF, false);
-    y.y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x.y, kWaveRol1, 0xF, 0xF, false);
-    y.z = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x.z, kWaveRol1, 0xF, 0xF, false);
-    y.w = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x.w, kWaveRol1, 0xF, 0xF, false);
-    return y;
-}
 
 // Slots per step of the realigning copy: with 3 KiB steps the routine needs
 // 66 VGPRs, which leaves the kernel, calling it, room to keep its own values

@@ -88,7 +88,7 @@ def test_reduce2_above_4GiB_sampled():
 @pytest.mark.parametrize("nsrc,n,offset,src_step", [
     (5, (1 << 29) + 515, 8, 0),    # 2 GiB + 2,060 B per source: one-wave tiles past the grid cap
     (3, (96 << 20) + 5, 4, 0),     # 384 MiB + 20 B per source: four-wave tiles, above the MALL size
-    (9, (1 << 28) + 261, 0, 4),    # 1 GiB + 1,044 B, sources 4/8/12/0 B off dst: realigning 1 KiB tiles past the cap
+    (5, (1 << 29) + 261, 0, 4),    # 2 GiB + 1,044 B, sources 4/8/12/0/4 B off dst: realigning 2 KiB tiles past the cap
 ])
 def test_reduce_multi_source_large_sampled(nsrc, n, offset, src_step):
     torch = require_gpu()
