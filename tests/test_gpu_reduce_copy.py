@@ -84,6 +84,25 @@ def test_reduce_copy_mixed_offsets_all_n(nsrc, dst_off, n):
     assert dbuf.guards_intact()
 
 
+@pytest.mark.parametrize("nsrc", [1, 3, 4, 16])
+@pytest.mark.parametrize("body_blocks", [1, 63, 64, 65, 127, 128, 129, 511, 512, 513])
+@pytest.mark.parametrize("tail", [0, 3])
+def test_reduce_copy_realigning_subtile_edges(nsrc, body_blocks, tail):
+    """Realigning path with the float4 body ending on, just before and just
+    after the edges of a wave's two 64-block sub-tiles and of a tile (512
+    blocks for four-wave workgroups, 128 for one-wave ones), two tiles in:
+    the block after a sub-tile's lane 63 comes from the next sub-tile, the
+    next wave or lane 63's own load, each clamped at the body's end."""
+    torch = require_gpu()
+    tile = 512 if nsrc <= 3 else 128
+    n = 4 * (2 * tile + body_blocks) + tail
+    offs = [(4 * (k + 1)) % 16 for k in range(nsrc)]
+    note(f"reduce_copy realigning nsrc={nsrc} n={n} source offsets {offs}")
+    got, exp, dbuf, _ = _run(torch, _sources(nsrc, n, seed=body_blocks + tail), n, dst_off=0, src_offs=offs)
+    assert oracle.first_mismatch(got, exp) == -1
+    assert dbuf.guards_intact()
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_reduce_copy_pointer_offsets_random(seed):
     torch = require_gpu()
