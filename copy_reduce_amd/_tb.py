@@ -27,7 +27,7 @@ EXPORTS = (
     "tb_reduce_copy_ex", "tb_batched_copy", "tb_batched_set_mode", "tb_spin_gate_arm", "tb_spin_gate_release",
     "tb_spin_gate_status", "tb_launch_info", "tb_shutdown",
     "tb_ring_create", "tb_ring_submit", "tb_ring_poll", "tb_ring_wait", "tb_ring_destroy",
-    "tb_time_next_launch", "tb_batched_set_max_workgroups",
+    "tb_time_next_launch", "tb_batched_set_max_workgroups", "tb_batched_copy_noalloc",
 )
 
 # torch ships its own HIP runtime under the same soname (libamdhip64.so.7) as
@@ -67,6 +67,7 @@ _SIGS = {
     "tb_reduce_copy": (ctypes.c_int, [_vp, _vp, _i32, _u64, _vp]),
     "tb_reduce_copy_ex": (ctypes.c_int, [_vp, _vp, _i32, _u64, _u32, _vp]),
     "tb_batched_copy": (ctypes.c_int, [_vp, _u32, _vp]),
+    "tb_batched_copy_noalloc": (ctypes.c_int, [_vp, _u32, _vp]),
     "tb_batched_set_mode": (ctypes.c_int, [_i32]),
     "tb_spin_gate_arm": (ctypes.c_int, [_u32, _vp]),
     "tb_spin_gate_release": (ctypes.c_int, []),
@@ -188,6 +189,10 @@ def tb_reduce_copy(dst_ptr: int, src_ptrs, nfloats: int, stream: int, memset_byt
 
 def tb_batched_copy(desc_dev_ptr: int, ncopies: int, stream: int) -> None:
     _check("tb_batched_copy", lib.tb_batched_copy(desc_dev_ptr, ncopies, stream))
+
+
+def tb_batched_copy_noalloc(desc_dev_ptr: int, ncopies: int, stream: int) -> None:
+    _check("tb_batched_copy_noalloc", lib.tb_batched_copy_noalloc(desc_dev_ptr, ncopies, stream))
 
 
 def tb_batched_set_mode(mode: int) -> None:

@@ -51,14 +51,14 @@ struct DeviceInfo {
 };
 
 std::mutex g_mu;
-DeviceInfo g_dev[64];
+DeviceInfo g_dev[tbk::kMaxDevices];
 
 int device_info(DeviceInfo *out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
         return hip_fail(e, "hipGetDevice");
-    if (dev < 0 || dev >= 64)
+    if (dev < 0 || dev >= tbk::kMaxDevices)
         return TB_ERR_INVALID;
     std::lock_guard<std::mutex> lk(g_mu);
     DeviceInfo &d = g_dev[dev];
@@ -324,6 +324,34 @@ int tb_batched_copy(const tb_copy_desc *desc_dev, uint32_t ncopies, void *stream
     if (e != hipSuccess)
         return hip_fail(e, "batched-copy launch");   // the epoch is not used up
     sc->epoch = epoch;
+    return TB_OK;
+}
+
+int tb_batched_copy_noalloc(const tb_copy_desc *desc_dev, uint32_t ncopies, void *stream) {
+    if (ncopies == 0)
+        return TB_OK;
+    if (desc_dev == nullptr || (reinterpret_cast<uintptr_t>(desc_dev) & 7u) != 0)
+        return TB_ERR_INVALID;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (tbh::capturing(s))
+        return TB_ERR_INVALID;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= tbk::kMaxDevices)
+        return TB_ERR_INVALID;
+    DeviceInfo info;
+    int rc = device_info(&info);
+    if (rc != TB_OK)
+        return rc;
+    const int mode = g_batched_mode.load(std::memory_order_relaxed);
+    const uint64_t wait_ticks =
+        mode == TB_BC_NORMAL ? (uint64_t)tbk::kBcSealWaitUs * info.wall_clock_khz / 1000u : 0u;
+    e = tbk::launch_batched_copy_static(desc_dev, ncopies, dev, info.cu_count, wait_ticks, mode == TB_BC_NO_PIECES,
+                                        s);
+    if (e != hipSuccess)
+        return hip_fail(e, "batched-copy launch on the static scratch");
     return TB_OK;
 }
 

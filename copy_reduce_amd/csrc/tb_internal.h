@@ -118,6 +118,17 @@ hipError_t launch_batched_copy(const tb_copy_desc *desc, uint32_t n, BcScratch *
 hipError_t launch_batched_copy_short(const tb_copy_desc *desc, uint32_t n, BcScratch *scratch, uint64_t epoch,
                                      int cu_count, hipStream_t stream, hipEvent_t done_event = nullptr);
 
+// Devices the library keeps per-device state for (ordinals 0 .. kMaxDevices-1).
+constexpr int kMaxDevices = 64;
+
+// As launch_batched_copy, on the static per-device scratch of
+// tb_batched_copy_noalloc instead of caller-given memory: no allocation.  The
+// first call on a device (which must be current) takes the scratch's device
+// address and clears it, synchronising `stream` once; epochs are numbered per
+// device under a lock.  Returns the first failing HIP status.
+hipError_t launch_batched_copy_static(const tb_copy_desc *desc, uint32_t n, int device, int cu_count,
+                                      uint64_t wait_ticks, bool no_pieces, hipStream_t stream);
+
 // ---- launch events -------------------------------------------------------------
 
 // The next kernel launched by the calling host thread records `start` when it

@@ -4,6 +4,7 @@
 // contraction, so there is no MFMA; both copies are HBM-bound streams and the
 // design is about keeping enough 16-byte loads in flight per CU.
 #include <atomic>
+#include <mutex>
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -929,6 +930,69 @@ hipError_t launch_batched_copy_short(const tb_copy_desc *desc, uint32_t n, BcScr
     if (g > cus * kBcMaxGridPerCu)
         g = cus * kBcMaxGridPerCu;
     return launch_bc(capped_grid(g), s, done_event, desc, n, scratch, epoch, 0u, 0u, 0u, 0u);
+}
+
+// ---- the batched copy over a static scratch (no allocation) --------------------
+//
+// tb_batched_copy_noalloc's scratch: one BcScratch per device, in the code
+// object's static device memory, so that no call allocates.  Its size does not
+// depend on the batch (long copies past the queue's capacity are copied by the
+// wave that found them), so any batch fits.  In host code `scratch` names a
+// host-side stand-in, not device memory: its device address is taken once per
+// device with hipGetSymbolAddress (with that device current) and only that
+// address is used afterwards, for kernel arguments and the clear.
+static __device__ __align__(256) unsigned char scratch[kBcScratchBytes];
+
+// Plain stores of zero over n16 16-byte words.
+__global__ __launch_bounds__(256) void bc_scratch_clear_kernel(u32x4 *p, uint32_t n16) {
+    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+    if (i < n16)
+        p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+namespace {
+struct StaticScratch {
+    std::mutex mu;           // orders epoch numbering and the launch it numbers
+    void *ptr = nullptr;     // device address of `scratch` on this device, once set up
+    uint64_t epoch = 0;      // epoch of the last launch enqueued on it
+};
+StaticScratch g_static_scratch[kMaxDevices];
+}  // namespace
+
+hipError_t launch_batched_copy_static(const tb_copy_desc *desc, uint32_t n, int device, int cu_count,
+                                      uint64_t wait_ticks, bool no_pieces, hipStream_t s) {
+    if (device < 0 || device >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    StaticScratch &st = g_static_scratch[device];
+    std::lock_guard<std::mutex> lk(st.mu);
+    if (st.ptr == nullptr) {
+        // Set-up, once per device (the caller made `device` current): the
+        // array's address, then a clear, finished before any launch uses it,
+        // so that launches on any stream find it zeroed.
+        void *p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255u) != 0)
+            return hipErrorInvalidSymbol;
+        constexpr uint32_t n16 = (uint32_t)(kBcScratchBytes / 16);
+        hipLaunchKernelGGL(bc_scratch_clear_kernel, dim3((n16 + 255) / 256), dim3(256), 0, s,
+                           static_cast<u32x4 *>(p), n16);
+        e = hipGetLastError();
+        if (e == hipSuccess)
+            e = hipStreamSynchronize(s);
+        if (e != hipSuccess)
+            return e;
+        st.ptr = p;
+    }
+    const uint64_t epoch = st.epoch + 1;
+    const int grid = batched_grid(n, cu_count);
+    const uint32_t resident = (uint32_t)(cu_count > 0 ? cu_count : 1) * kBcResidentWavesPerCu;
+    const hipError_t e = launch_bc(grid, s, nullptr, desc, n, static_cast<BcScratch *>(st.ptr), epoch,
+                                   batched_scanners(n, grid), wait_ticks, resident, no_pieces ? 1u : 0u);
+    if (e == hipSuccess)
+        st.epoch = epoch;   // a failed launch does not use up its epoch
+    return e;
 }
 
 // ============================================================================

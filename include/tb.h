@@ -206,6 +206,32 @@ int tb_reduce_copy_ex(float *dst, const float *const *srcs, int32_t nsrc,
 int tb_batched_copy(const tb_copy_desc *desc_dev, uint32_t ncopies, void *stream);
 
 /*
+ * tb_batched_copy without allocation, for callers that cannot allocate device
+ * memory (tight serving loops, harnesses that forbid hipMalloc): the same
+ * kernel and the same result as tb_batched_copy, with its scratch in a static
+ * device array of the library (131,840 bytes per device, held until the
+ * process ends) instead of memory allocated per (device, stream).  No call
+ * allocates: the first call on a device takes the array's address and clears
+ * it, synchronising `stream` once; later calls only enqueue the kernel.  The
+ * scratch's size does not depend on the batch (long copies beyond its queue
+ * are copied by the wave that finds them), so every ncopies that
+ * tb_batched_copy takes is taken here.
+ * Every call on one device shares that device's array: calls whose kernels can
+ * overlap in time on one device (different streams not ordered by the caller,
+ * or this call beside itself on another thread's unordered stream) race and
+ * give unspecified bytes.  Calls on one stream are ordered and safe, from any
+ * number of host threads.  Launches are numbered per device, and the array
+ * keeps the last launch's state, which the next launch expects: nothing needs
+ * clearing between calls.  Refused on a stream under graph capture, as
+ * tb_batched_copy.
+ * Errors: as tb_batched_copy (TB_ERR_INVALID for a NULL or misaligned
+ * desc_dev with ncopies > 0, a stream under capture, or a device ordinal of 64
+ * or more; TB_ERR_HIP if the array's address, its clear or the launch fails);
+ * never TB_ERR_NOMEM.
+ */
+int tb_batched_copy_noalloc(const tb_copy_desc *desc_dev, uint32_t ncopies, void *stream);
+
+/*
  * Test hook for the batched copy's recovery path (process-wide; affects
  * launches made after the call).  Long copies go through a queue whose pieces
  * the waves share once every scanning workgroup has published; the wait for

@@ -187,6 +187,9 @@ def test_batched_copy_argument_checks():
     assert _st("tb_batched_copy", None, 5, None) == tb.TB_ERR_INVALID
     assert _st("tb_batched_copy", 0x1004, 5, None) == tb.TB_ERR_INVALID                  # not 8-byte aligned
     assert _st("tb_batched_copy", None, 0, None) == tb.TB_OK
+    assert _st("tb_batched_copy_noalloc", None, 5, None) == tb.TB_ERR_INVALID
+    assert _st("tb_batched_copy_noalloc", 0x1004, 5, None) == tb.TB_ERR_INVALID
+    assert _st("tb_batched_copy_noalloc", None, 0, None) == tb.TB_OK
 
 
 def test_timing_hook_needs_no_device():
