@@ -34,6 +34,8 @@ sys.path.insert(0, ROOT)
 METRIC = "HBM GB/s & % of peak (rotated reduce-copy); GB/s + copies/s (batched scatter)"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 GATE_TIMEOUT_MS = 20000
+DST_ROTATE_BYTES = 1 << 30      # the bench step's reduce-copy destination rotates over this many bytes
+BATCH_DST_ROTATE_BYTES = 512 << 20   # and the batched copy's destination pools over this many payload bytes
 CPU_BUDGET_S = 10.0             # single-core work of the cpu_baseline leg
 
 
@@ -125,28 +127,6 @@ def run_launch_events(torch, tb, stream, launches):
     return [st[j].elapsed_time(sp[j]) for j in range(len(launches))], st[0].elapsed_time(sp[-1])
 
 
-def reduce_copy_mall_flushed(torch, tb, stream, launches):
-    """Each launch after an untimed 1 GiB streaming copy (which evicts the
-    256 MB memory-side cache), timed by its own launch events: per-launch ms.
-    The flush is the library's one-source copy, whose device-scope stores
-    allocate in that cache; nontemporal stores would leave it in place."""
-    fa = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
-    fb = torch.empty_like(fa)
-    out = []
-    for fn in launches:
-        tb.tb_reduce_copy(int(fb.data_ptr()), [int(fa.data_ptr())], fa.numel(), stream.cuda_stream)
-        st, sp = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        st.record(stream)
-        sp.record(stream)                # a first record creates the events
-        tb.tb_time_next_launch(st.cuda_event, sp.cuda_event)
-        fn()
-        torch.cuda.synchronize()
-        out.append(st.elapsed_time(sp))
-    del fa, fb
-    torch.cuda.empty_cache()
-    return out
-
-
 def device_record(torch, tb):
     """Name, CU count and the partition modes the measurement ran under (the
     cache behaviour rotation guards against depends on them)."""
@@ -181,24 +161,32 @@ def setup_reduce(torch, w):
     return rs, dst
 
 
-def setup_batch(torch, tb, batch, rotate_bytes):
+def setup_batch(torch, tb, batch, rotate_bytes, dst_rotate_bytes=0):
     """K_b source replicas (the slice-count rule over the batch's source bytes)
-    and one descriptor array per replica; pool pre-filled with 0xA5."""
+    and K_p destination pools (the same rule over dst_rotate_bytes; one pool
+    when it is 0), each pool pre-filled with 0xA5; one descriptor array per
+    (replica, pool).  Iteration i reads replica i mod K_b and writes pool
+    i mod K_p."""
     import workloads as wl
     from copy_reduce_amd.torch_api import make_desc
     batch.check()
     kb = tb.tb_num_slices(batch.total_bytes, rotate_bytes)
+    kp = tb.tb_num_slices(batch.total_bytes, dst_rotate_bytes)
     stride = tb.tb_slice_stride(batch.src_bytes)
+    pstride = tb.tb_slice_stride(batch.pool_bytes)
     src = torch.empty(max(1, kb * stride), dtype=torch.uint8, device="cuda")
     host = torch.from_numpy(batch.payload).pin_memory()
     for r in range(kb):
         src[r * stride:r * stride + batch.src_bytes].copy_(host, non_blocking=True)
-    pool = torch.full((batch.pool_bytes,), wl.POOL_FILL, dtype=torch.uint8, device="cuda")
-    base = int(src.data_ptr())
-    descs = {base + r * stride: make_desc(batch.desc, base + r * stride, int(pool.data_ptr()))
-             for r in range(kb)}
+    pools = torch.full((kp * pstride,), wl.POOL_FILL, dtype=torch.uint8, device="cuda")
+    base, pbase = int(src.data_ptr()), int(pools.data_ptr())
+    descs = {(base + r * stride, pbase + p * pstride): make_desc(batch.desc, base + r * stride, pbase + p * pstride)
+             for r in range(kb) for p in range(kp)}
     torch.cuda.synchronize()
-    return {"kb": kb, "stride": stride, "src": src, "pool": pool, "descs": descs, "base": base}
+    return {"kb": kb, "stride": stride, "src": src, "descs": descs, "base": base,
+            "kp": kp, "pstride": pstride, "pools": pools, "pbase": pbase,
+            "pool_views": [pools[p * pstride:p * pstride + batch.pool_bytes] for p in range(kp)],
+            "pool": pools[:batch.pool_bytes]}
 
 
 def replica_of(tb, b, i):
@@ -208,8 +196,17 @@ def replica_of(tb, b, i):
 
 
 def batch_desc_for(tb, b, i):
-    """Descriptor array read by iteration i."""
-    return b["descs"][b["base"] + replica_of(tb, b, i) * b["stride"]]
+    """Descriptor array of iteration i: source replica and destination pool by
+    the library's rotation (slice i mod K)."""
+    (src,) = tb.tb_rotate_sources([b["base"]], b["stride"], b["kb"], i)
+    (pool,) = tb.tb_rotate_sources([b["pbase"]], b["pstride"], b["kp"], i)
+    return b["descs"][(src, pool)]
+
+
+def pools_written(b, first, last):
+    """The destination pools iterations first .. last - 1 wrote."""
+    kp = b["kp"]
+    return [b["pool_views"][p] for p in sorted({(i % kp + kp) % kp for i in range(first, last)})]
 
 
 # ---------------------------------------------------------------------------
@@ -222,12 +219,24 @@ def main_line(args, torch, tb, wl):
     w = wl.REDUCE_CONFIGS["c2_reduce2_256MiB_rot"]
     rs, dst = setup_reduce(torch, w)
     batch = wl.batch_c4()
-    b = setup_batch(torch, tb, batch, wl.DEFAULT_ROTATE_BYTES)
-    dst_ptr = int(dst.data_ptr())
+    b = setup_batch(torch, tb, batch, wl.DEFAULT_ROTATE_BYTES, BATCH_DST_ROTATE_BYTES)
+    # The destination rotates too, by the slice rule over DST_ROTATE_BYTES: at
+    # 256 MiB per buffer the source rule gives K = 1, and a fixed 256 MiB
+    # destination stays in the 256 MB memory-side cache, which then absorbs
+    # its rewrites; over K_d slices every launch writes lines no recent launch
+    # wrote, so the timed rate is the HBM rate.
+    kd = tb.tb_num_slices(rs.num_bytes, DST_ROTATE_BYTES)
+    dsts = torch.zeros(kd * rs.stride // 4, dtype=torch.float32, device="cuda")
+    dst_base = int(dsts.data_ptr())
+    dst_fixed = int(dst.data_ptr())
 
-    def rc(i):
+    def dst_for(i):
+        return tb.tb_rotate_sources([dst_base], rs.stride, kd, i)[0]
+
+    def rc(i, fixed=False):
         ptrs = rs.pointers(i)                      # rotation: before the launch, untimed work
-        return lambda: tb.tb_reduce_copy(dst_ptr, ptrs, w.nfloats, sh)
+        d = dst_fixed if fixed else dst_for(i)
+        return lambda: tb.tb_reduce_copy(d, ptrs, w.nfloats, sh)
 
     def bc(i):
         d = batch_desc_for(tb, b, i)
@@ -246,7 +255,15 @@ def main_line(args, torch, tb, wl):
     total_ms, wall = run_whole(torch, tb, stream, launches)
     ms, total_ms_launch_events = run_launch_events(torch, tb, stream, launches)
     rc_ms, bc_ms = ms[0::2], ms[1::2]
-    rc_flushed_ms = reduce_copy_mall_flushed(torch, tb, stream, [rc(i) for i in range(args.steps)])
+    # the pages' literal protocol beside it: the same steps with one fixed destination
+    for i in range(-args.warmup, 0):
+        rc(i, fixed=True)()
+        bc(i)()
+    fixed = []
+    for i in range(args.steps):
+        fixed += [rc(i, fixed=True), bc(i)]
+    ms_fixed, _ = run_launch_events(torch, tb, stream, fixed)
+    rc_fixed_ms = ms_fixed[0::2]
 
     rc_bytes, bc_bytes = w.algorithmic_bytes, batch.algorithmic_bytes
     step_bytes = rc_bytes + bc_bytes
@@ -272,13 +289,15 @@ def main_line(args, torch, tb, wl):
         "data": "synthetic",
         "config": {
             "workload": "rotated 2-source fp32 reduce-copy, 256 MiB per buffer (67,108,864 floats, "
-                        "PrepSrcValue sources, SRC_ROTATE_BYTES=256 MiB -> K=1) + batched scattered copy "
+                        "PrepSrcValue sources, SRC_ROTATE_BYTES=256 MiB -> K=1; destination rotated over "
+                        f"K_d={kd} slices, 1 GiB) + batched scattered copy "
                         "of 47,520 copies log-uniform 64 B-16 KiB into random 16 KiB slots of a 4 GiB pool "
-                        f"(K_b={b['kb']} source replicas), one of each per step",
+                        f"(K_b={b['kb']} source replicas, K_p={b['kp']} destination pools), one of each per step",
             "reduce_copy": {"nsrc": w.nsrc, "nfloats": w.nfloats, "rotate_bytes": w.rotate_bytes, "k": rs.k,
-                            "bytes_per_launch": rc_bytes},
+                            "dst_rotate_bytes": DST_ROTATE_BYTES, "k_dst": kd, "bytes_per_launch": rc_bytes},
             "batched_copy": {"ncopies": batch.ncopies, "payload_bytes": batch.total_bytes,
-                             "bytes_per_launch": bc_bytes, "replicas": b["kb"]},
+                             "bytes_per_launch": bc_bytes, "replicas": b["kb"], "dst_rotate_bytes":
+                             BATCH_DST_ROTATE_BYTES, "pools": b["kp"]},
             "launch": info,
         },
         "device": device_record(torch, tb),
@@ -286,11 +305,12 @@ def main_line(args, torch, tb, wl):
             "reduce_copy": {"ms_mean": round(rc_mean, 5), "ms_min": round(min(rc_ms), 5),
                             "ms_max": round(max(rc_ms), 5), "gbps": round(rc_gbps, 1),
                             "frac_of_peak": round(rc_gbps / HBM_PEAK_GBPS, 4),
-                            "mall_flushed": {
-                                "note": "each launch preceded by an untimed 1 GiB copy that evicts the 256 MB "
-                                        "memory-side cache; not the pages' method, the rate without cache help",
-                                "ms_mean": round(statistics.mean(rc_flushed_ms), 5),
-                                "frac_of_peak": round(rc_bytes / (statistics.mean(rc_flushed_ms) * 1e-3) / 1e9
+                            "fixed_dst": {
+                                "note": "the same steps with one fixed destination, as the pages time it: the "
+                                        "256 MiB destination then stays in the 256 MB memory-side cache, which "
+                                        "absorbs part of its rewrites (not an HBM rate)",
+                                "ms_mean": round(statistics.mean(rc_fixed_ms), 5),
+                                "frac_of_peak": round(rc_bytes / (statistics.mean(rc_fixed_ms) * 1e-3) / 1e9
                                                       / HBM_PEAK_GBPS, 4)}},
             "batched_copy": {"ms_mean": round(bc_mean, 5), "ms_min": round(min(bc_ms), 5),
                              "ms_max": round(max(bc_ms), 5), "gbps": round(bc_gbps, 1),
@@ -317,15 +337,19 @@ def main_line(args, torch, tb, wl):
     }
 
     if not args.no_cpu_baseline:
-        line["cpu_baseline"], line["validated"] = cpu_baseline(torch, w, batch, dst, b["pool"])
+        written = sorted({(i % kd + kd) % kd for i in range(-args.warmup, args.steps)})
+        views = [dsts[s * rs.stride // 4:s * rs.stride // 4 + w.nfloats] for s in written] + [dst]
+        line["cpu_baseline"], line["validated"] = cpu_baseline(torch, w, batch, views,
+                                                               pools_written(b, -args.warmup, args.steps))
     print(json.dumps(line), flush=True)
     return line
 
 
-def cpu_baseline(torch, w, batch, dst, pool):
+def cpu_baseline(torch, w, batch, dsts, pools):
     """The oracle, as it stands, timed on one host core over the full step,
     repeated for about CPU_BUDGET_S seconds (median); also checks the GPU
-    results of the timed run against it."""
+    results of the timed run against it: every destination slice the
+    reduce-copy wrote, and the whole pool."""
     import numpy as np
 
     import oracle
@@ -341,8 +365,8 @@ def cpu_baseline(torch, w, batch, dst, pool):
     rc_s, bc_s = statistics.median(t_rc), statistics.median(t_bc)
     step_bytes = w.algorithmic_bytes + batch.algorithmic_bytes
     validated = {
-        "reduce_copy": oracle.first_mismatch(dst.cpu().numpy(), exp) == -1,
-        "batched_copy": oracle.first_mismatch(pool.cpu().numpy(), image) == -1,
+        "reduce_copy": all(oracle.first_mismatch(d.cpu().numpy(), exp) == -1 for d in dsts),
+        "batched_copy": all(oracle.first_mismatch(p.cpu().numpy(), image) == -1 for p in pools),
     }
     cpu = {
         "value": round(step_bytes / (rc_s + bc_s) / 1e9, 3),
@@ -464,8 +488,11 @@ def suite(args, torch, tb, wl):
         torch.cuda.empty_cache()
         return out
 
-    def batch_line(batch, rotate_bytes, tag):
-        b = setup_batch(torch, tb, batch, rotate_bytes)
+    def batch_line(batch, rotate_bytes, tag, dst_rotate_bytes=0):
+        """dst_rotate_bytes: rotate the destination pool too (K_p pools by the
+        slice rule), so no launch rewrites lines a recent launch left in the
+        memory-side cache; not the pages' method (they rotate sources only)."""
+        b = setup_batch(torch, tb, batch, rotate_bytes, dst_rotate_bytes)
         # The library creates a stream's scratch on its first call there: one
         # descriptor of zero bytes before the cold launch keeps that allocation
         # out of the cold figure (the kernel copies nothing for it).
@@ -488,7 +515,7 @@ def suite(args, torch, tb, wl):
         mean = statistics.mean(ms)
         gbps = batch.algorithmic_bytes / (mean * 1e-3) / 1e9
         out = {"config": f"{batch.name}_{tag}", "ncopies": batch.ncopies, "payload_bytes": batch.total_bytes,
-               "replicas": b["kb"], "ms_mean": round(mean, 5), "ms_min": round(min(ms), 5),
+               "replicas": b["kb"], "pools": b["kp"], "ms_mean": round(mean, 5), "ms_min": round(min(ms), 5),
                "ms_max": round(max(ms), 5), "ms_cold": round(cold_ms[0], 5), "gbps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
                "copies_per_s": round(batch.ncopies / (mean * 1e-3), 1)}
         out.update(_kernel_and_loop(batch.algorithmic_bytes, statistics.mean(kms), whole, args.steps))
@@ -509,6 +536,10 @@ def suite(args, torch, tb, wl):
         ("c4_scatter_47520_rotated", lambda: batch_line(wl.batch_c4(), wl.DEFAULT_ROTATE_BYTES, "rotated")),
         ("c4_scatter_47520_control", lambda: batch_line(wl.batch_c4(), 0, "control")),
         ("c5_mixed_kv_11044_rotated", lambda: batch_line(wl.batch_c5(), wl.DEFAULT_ROTATE_BYTES, "rotated")),
+        ("c4_scatter_47520_rotated_dstrot", lambda: batch_line(wl.batch_c4(), wl.DEFAULT_ROTATE_BYTES,
+                                                               "rotated_dstrot", BATCH_DST_ROTATE_BYTES)),
+        ("c5_mixed_kv_11044_rotated_dstrot", lambda: batch_line(wl.batch_c5(), wl.DEFAULT_ROTATE_BYTES,
+                                                                "rotated_dstrot", BATCH_DST_ROTATE_BYTES)),
     ]
     for nbytes in wl.SWEEP_BYTES:
         for rot in (True, False):

@@ -261,13 +261,13 @@ int tb_reduce_copy_ex(float *dst, const float *const *srcs, int32_t nsrc, uint64
     a.head = (uint32_t)head;
     a.nvec = (nfloats - head) / 4;
     a.tail = (uint32_t)((nfloats - head) % 4);
-    // Each source's offset from 16-byte alignment at the element that lines
-    // up with dst's first aligned one; all zero takes the plain vector path.
+    // The vector path needs every source to agree with dst modulo 16 (its
+    // element `head` then starts a 16-byte block); otherwise the unaligned
+    // kernel reads each source at its own 4-byte alignment.
     bool vector_path = true;
     for (int32_t k = 0; k < nsrc; k++) {
         const uintptr_t body = reinterpret_cast<uintptr_t>(a.src[k]) + 4u * head;
-        a.shift[k] = (uint8_t)((body & 15u) / 4u);
-        if (a.shift[k] != 0)
+        if ((body & 15u) != 0)
             vector_path = false;
     }
 

@@ -29,17 +29,14 @@ struct ReduceArgs {
     uint32_t head;
     uint32_t tail;
     uint32_t fill;       // 32-bit memset pattern for nsrc == 0
-    // Per source, (address of its element `head`) mod 16, in floats: 0 when
-    // the source agrees with dst modulo 16.
-    uint8_t shift[TB_MAX_SRCS];
 };
 
 // Workgroups the reduce-copy kernel is launched with.
 int reduce_grid(uint64_t nfloats, int nsrc, bool vector_path, int cu_count);
 
-// Enqueue the reduce-copy for nsrc sources (head/nvec/tail/shift filled in by
-// the caller).  vector_path: every source agrees with dst modulo 16 (every
-// shift is 0); otherwise the realigning kernel runs.
+// Enqueue the reduce-copy for nsrc sources (head/nvec/tail filled in by the
+// caller).  vector_path: every source agrees with dst modulo 16; otherwise the
+// unaligned kernel runs.
 hipError_t launch_reduce_copy(const ReduceArgs &args, int nsrc, bool vector_path,
                               int cu_count, hipStream_t stream);
 

@@ -47,61 +47,50 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(uint64_t base, uin
                                              0x00020000);
 }
 
-// Tile shape of the vector path, by number of sources.  One tile per
-// workgroup.  Measured on MI355X (sources of 64 MiB rotated over 4 slices,
-// median of 3 runs): up to three sources, four-wave workgroups of 1 (N <= 2)
-// or 2 (N = 3) float4s per thread reach 84-94%; from four sources up,
-// one-wave workgroups of 2 float4s per thread per source beat them by 2-7
-// points (N = 4: 84.6% against 82.3%; N = 6: 83.6% against 77.1%; N = 16:
-// 81.3% against 77.1%).  At that register footprint a four-wave workgroup
-// must find four free wave slots on one CU at once; a one-wave workgroup
-// fills any free slot.
-constexpr int rc_block_of(int nsrc) { return nsrc >= 4 ? 64 : kRcBlock; }
-constexpr int rc_unroll_of(int nsrc) { return nsrc <= 2 ? 1 : 2; }
-// The realigning path gives each wave two contiguous sub-tiles of 64 blocks
-// per source, whatever the source count (see rc_shift_kernel).
-constexpr int rc_shift_unroll_of(int) { return 2; }
-
-template <int N>
-constexpr bool rc_xcd_map() {
-    return N <= 2;
-}
+// Tile shape of the reduce-copy, by number of sources: one float4 per thread
+// and source, one tile per workgroup, tiles dealt in address order (workgroup
+// b takes tile b), so at any moment the whole chip works on one compact
+// window of each buffer.  Workgroups are one wave for up to two sources (a
+// 1 KiB tile per buffer) and two waves from three up (2 KiB).  Measured on
+// MI355X with every launch writing a destination no recent launch wrote
+// (rotated over 1 GiB), 3 warmups + 10 launches, 2-4 runs: a 512 MiB copy
+// 85-86% of HBM peak against 83% with four-wave workgroups whose tiles each
+// XCD walked in its own contiguous eighth; two sources of 256 MiB 84-85%
+// against 82%; three sources 77% against 74% (four-wave tiles of two float4
+// per thread); four to sixteen sources within a point of one-wave tiles of
+// two float4 per thread.  Larger tiles per wave were slower at every source
+// count: two, four, eight and sixteen float4 per thread cost a copy 5-10
+// points, and keeping only two or three sources' loads in flight at once
+// (a rolling order) changed eight and sixteen sources by under a point.
+constexpr int rc_block_of(int nsrc) { return nsrc <= 2 ? 64 : 128; }
+// How the vector path reads a tile: through one buffer resource per source on
+// the tile's scalar base (the thread's byte offset the only vector operand),
+// or with global loads of 64-bit per-thread addresses.  Measured on MI355X
+// (64 MiB per source, 3 runs each): buffer loads are 0.6-4 points faster
+// from two to eight sources (three: 78% against 75%, four: 80% against 76%)
+// and 0.3-1.3 points slower for one, twelve and sixteen.
+constexpr bool rc_buffer_loads(int nsrc) { return nsrc >= 2 && nsrc <= 8; }
+// Workgroup size of the unaligned path (some source off dst's 16-byte
+// alignment): two waves, one float4 per thread and source, whatever the
+// source count.  Measured with sources 4 or 8 bytes off: 81% for a 512 MiB
+// copy and two sources of 256 MiB against 79% and 76% with one-wave
+// workgroups.
+constexpr int kRcUnalignedBlock = 128;
 
 // Sources are streamed once per launch: nontemporal loads (without them the
 // kernel measured 73% of peak instead of 92%).  Results are written with
-// device-scope (sc1) stores, through L2 to the memory side.  Measured on
-// MI355X, two sources of 256 MiB: with the destination resident in the 256 MB
-// memory-side cache (MALL) across launches (a fixed destination, as timed by
-// the pages) sc1 stores reach 88-93% against 77% for nontemporal ones and 83%
-// for plain ones.  Above the MALL's size nontemporal system-scope stores
-// (nt sc0 sc1) gain nothing either: one-source copies of 512 MiB ran at
-// 82-84% with both, and the first launch after preparation 85% with sc1
-// against 82%.  Nontemporal stores and loads also leave lines already in the
-// MALL in place: a 1 GiB copy made of them, run between launches to evict
-// it, left a 256 MiB destination resident (91% against 78% after a copy with
-// sc1 stores).
-constexpr int kRcStorePol = kPolSc1;
+// nontemporal system-scope stores (nt sc0 sc1), which do not allocate in the
+// 256 MB memory-side cache (MALL): the kernel's rate is then the same whether
+// or not the destination was written recently.  Device-scope stores (sc1)
+// allocate there, and a fixed destination rewritten launch after launch (the
+// pages' timing) then reads 92-93% for two sources of 256 MiB, against 81-82%
+// once the destination rotates over 1 GiB, where these stores reach 84-85%
+// under either timing.  Stores that allocate in the MALL also leave dirty
+// lines that a following kernel pays for: behind such batched-copy stores the
+// next 256 MiB reduce-copy fell from 81% to 67%.
+constexpr int kRcStorePol = kPolNt | kPolSc0 | kPolSc1;
 __device__ __forceinline__ f32x4 rc_load(const gf32x4 *p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ float rc_load(const gf32 *p) { return __builtin_nontemporal_load(p); }
-
-// Workgroup b runs on XCD b % 8 (round-robin dispatch).  xcd_tile gives each
-// XCD one contiguous eighth of the tiles, walked in order, instead of every
-// eighth tile.  `v` is the virtual block index in [0, 8 * ceil(ntiles / 8));
-// returns false for the few virtual blocks that have no tile.  A bijection
-// onto [0, ntiles).  Measured on MI355X (cold destination): +3 points for two
-// sources, equal for one, and 2-7 points slower from three sources up (eight
-// regions times N + 1 streams at once), so it is used only for N <= 2.
-__device__ __forceinline__ bool xcd_tile(uint64_t v, uint64_t ntiles, uint64_t *tile) {
-    const uint64_t q = ntiles >> 3, r = ntiles & 7;
-    const uint64_t x = v & 7, k = v >> 3;
-    const uint64_t count = q + (x < r ? 1 : 0);
-    if (k >= count)
-        return false;
-    *tile = x * q + (x < r ? x : r) + k;
-    return true;
-}
-
-__device__ __forceinline__ uint64_t virtual_blocks(uint64_t ntiles) { return (ntiles + 7) & ~(uint64_t)7; }
 
 // Fixed-order scalar sum of element j (used for the unaligned head and tail).
 template <int N>
@@ -113,64 +102,45 @@ __device__ __forceinline__ float rc_sum_scalar(const ReduceArgs &a, uint64_t j) 
     return acc;
 }
 
-// Vector path: every pointer is congruent to dst modulo 16.  Tiles of
-// BS threads x U float4s; each thread loads U float4s from every source
-// before the first addition, so N * U 16-byte loads per thread are in flight.
-// gridDim.x is a multiple of 8 (see reduce_grid), so the grid-stride step
-// keeps a workgroup on its XCD's share of the tiles.
+// Vector path: every pointer is congruent to dst modulo 16.  Tile t is the
+// BS float4s t * BS .. t * BS + BS - 1 of every buffer, one per thread; each
+// thread loads its float4 from every source before the first addition, so N
+// 16-byte loads per thread are in flight.
 template <int N>
 __global__ __launch_bounds__(rc_block_of(N)) void rc_vec_kernel(ReduceArgs a) {
     constexpr int BS = rc_block_of(N);
-    constexpr int U = rc_unroll_of(N);
-    constexpr uint64_t kTile = (uint64_t)BS * U;
     const uint64_t nvec = a.nvec;
-    const uint64_t ntiles = (nvec + kTile - 1) / kTile;
+    const uint64_t ntiles = (nvec + BS - 1) / BS;
     const gf32x4 *src[N];
 #pragma unroll
     for (int k = 0; k < N; k++)
         src[k] = (const gf32x4 *)(a.src[k] + a.head);
 
-    const uint64_t vend = rc_xcd_map<N>() ? virtual_blocks(ntiles) : ntiles;
-    for (uint64_t v = blockIdx.x; v < vend; v += gridDim.x) {
-        uint64_t t = v;
-        if (rc_xcd_map<N>() && !xcd_tile(v, ntiles, &t))
-            continue;
-        const uint64_t base = t * kTile;
-        const uint64_t i0 = base + threadIdx.x;
-        if (base + kTile <= nvec) {
-            f32x4 val[N][U];
+    for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const uint64_t base = t * BS;
+        // dst blocks in this tile: BS, or fewer in the last, partial tile,
+        // where threads past nvec do nothing (a wave-uniform branch)
+        const uint32_t nblk = (uint32_t)(nvec - base < (uint64_t)BS ? nvec - base : (uint64_t)BS);
+        if (threadIdx.x < nblk) {
+            f32x4 val[N];
 #pragma unroll
-            for (int k = 0; k < N; k++)
-#pragma unroll
-                for (int u = 0; u < U; u++)
-                    val[k][u] = rc_load(src[k] + i0 + (uint64_t)u * BS);
-            const __amdgpu_buffer_rsrc_t out =
-                buffer_over(reinterpret_cast<uint64_t>(a.dst + a.head) + base * 16, (uint32_t)(kTile * 16));
-#pragma unroll
-            for (int u = 0; u < U; u++) {
-                f32x4 acc = val[0][u];
-#pragma unroll
-                for (int k = 1; k < N; k++)
-                    acc = acc + val[k][u];
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), out, threadIdx.x * 16,
-                                                       u * BS * 16, kRcStorePol);
+            for (int k = 0; k < N; k++) {
+                if constexpr (rc_buffer_loads(N))
+                    val[k] = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                   buffer_over(reinterpret_cast<uint64_t>(src[k]) + base * 16, nblk * 16u),
+                                   threadIdx.x * 16, 0, kPolNt));
+                else
+                    val[k] = rc_load(src[k] + base + threadIdx.x);
             }
-        } else {
-            // the last, partial tile: stores past nvec are dropped by the range check
+            f32x4 acc = val[0];
+#pragma unroll
+            for (int k = 1; k < N; k++)
+                acc = acc + val[k];
             const __amdgpu_buffer_rsrc_t out =
-                buffer_over(reinterpret_cast<uint64_t>(a.dst + a.head) + base * 16, (uint32_t)((nvec - base) * 16));
-#pragma unroll
-            for (int u = 0; u < U; u++) {
-                const uint64_t i = i0 + (uint64_t)u * BS;
-                if (i < nvec) {
-                    f32x4 acc = rc_load(src[0] + i);
-#pragma unroll
-                    for (int k = 1; k < N; k++)
-                        acc = acc + rc_load(src[k] + i);
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), out,
-                                                           (threadIdx.x + u * BS) * 16, 0, kRcStorePol);
-                }
-            }
+                buffer_over(reinterpret_cast<uint64_t>(a.dst + a.head) + base * 16, nblk * 16u);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), out, threadIdx.x * 16, 0,
+                                                   kRcStorePol);
         }
     }
 
@@ -187,18 +157,6 @@ __global__ __launch_bounds__(rc_block_of(N)) void rc_vec_kernel(ReduceArgs a) {
             d[j] = rc_sum_scalar<N>(a, j);
         }
     }
-}
-
-// The four floats starting `r` floats into the 32 bytes (x, y): the source's
-// elements that line up with one 16-byte block of dst.  r is the same for
-// every thread, so the selects cost a few VALU operations and no branches.
-__device__ __forceinline__ f32x4 rc_funnel(u32x4 x, u32x4 y, uint32_t r) {
-    u32x4 o;
-    o.x = r == 0 ? x.x : (r == 1 ? x.y : (r == 2 ? x.z : x.w));
-    o.y = r == 0 ? x.y : (r == 1 ? x.z : (r == 2 ? x.w : y.x));
-    o.z = r == 0 ? x.z : (r == 1 ? x.w : (r == 2 ? y.x : y.y));
-    o.w = r == 0 ? x.w : (r == 1 ? y.x : (r == 2 ? y.y : y.z));
-    return __builtin_bit_cast(f32x4, o);
 }
 
 // Lane i's copy of lane i + 1's x (DPP wave shift left by one lane); lane 63
@@ -225,84 +183,49 @@ __device__ __forceinline__ u32x4 rol1_lane(u32x4 x) {
     return y;
 }
 
-// Realigning path: every pointer is 4-byte aligned and some source disagrees
-// with dst modulo 16.  dst is cut as on the vector path (head floats, float4
-// body, tail floats).  Source k's element for dst body block i lies `shift[k]`
-// floats into the source's aligned 16-byte block i, so a thread needs the
-// source's aligned blocks i and i + 1.  It loads block i (a nontemporal
-// 16-byte load, as on the vector path) and takes block i + 1 from the next
-// lane with a DPP wave shift.  A wave covers two contiguous sub-tiles of 64
-// blocks, so lane 63's block i + 1 in the first is lane 0's block in the
-// second (a DPP wave rotate); only the second's lane 63 loads it.  The four
-// floats at the offset are then selected in registers and summed in the
-// fixed order.  Block indexes are clamped to the last block that holds one
-// of the tile's source elements (the block past the tile's last one when
-// shift[k] > 0), so only whole 16-byte blocks holding a source element are
-// read; a lane past the tile's end re-reads a block and stores nothing.
-// Measured at 256 MiB per buffer, every source 4 or 8 bytes off dst: 93%
-// (one source), 89-90% (two), 79-80% (four), 75-76% (eight), 73% (sixteen).
-// One sub-tile per wave, each lane 63 loading its own block i + 1, measured
-// 81%, 89%, 80-81%, 76-77% and 70%: the single-lane load per wave and source
-// cost one source 12 points.  The per-float path this replaced ran at 74%,
-// 79%, 78%, 72% and 66%; loading block i + 1 as well instead of the DPP shift,
-// 73%, 79% and 59% for one, two and four sources.
-template <int N>
-__global__ __launch_bounds__(rc_block_of(N)) void rc_shift_kernel(ReduceArgs a) {
-    constexpr int BS = rc_block_of(N);
-    constexpr int U = rc_shift_unroll_of(N);
-    constexpr uint64_t kTile = (uint64_t)BS * U;
-    const uint64_t nvec = a.nvec;
-    const uint64_t ntiles = (nvec + kTile - 1) / kTile;
+// A float4 at 4-byte alignment: loads through it are single 16-byte loads at
+// any 4-byte-aligned address (gfx950 supports unaligned global accesses; the
+// memory system splits a lane's access where it crosses a cache line).
+typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
+typedef __attribute__((address_space(1))) f32x4u gf32x4u;
 
-    const uint64_t vend = rc_xcd_map<N>() ? virtual_blocks(ntiles) : ntiles;
-    for (uint64_t v = blockIdx.x; v < vend; v += gridDim.x) {
-        uint64_t t = v;
-        if (rc_xcd_map<N>() && !xcd_tile(v, ntiles, &t))
-            continue;
-        const uint64_t base = t * kTile;
-        const uint32_t nblk = (uint32_t)(nvec - base < kTile ? nvec - base : kTile);   // dst blocks here
-        // This wave's U sub-tiles of 64 blocks are contiguous, so lane 63's
-        // block i + 1 in sub-tile u is lane 0's block in sub-tile u + 1; only
-        // the last sub-tile's lane 63 loads it.
-        const uint32_t lane = threadIdx.x & 63u;
-        const uint32_t wbase = (threadIdx.x >> 6) * (uint32_t)(U * 64);
-        u32x4 xs[N][U], zs[N];
+// Unaligned path: every pointer is 4-byte aligned and some source disagrees
+// with dst modulo 16.  dst is cut as on the vector path (head floats, float4
+// body, tail floats); the thread that writes dst body block i reads, from
+// every source, the 16 bytes holding that source's four elements for it, with
+// one 16-byte load at the elements' own (4-byte) alignment.  Every load reads
+// only the source's own elements, so nothing outside the source is touched.
+// Measured at 256 MiB per buffer against an earlier form that loaded aligned
+// 16-byte blocks and realigned them in registers (DPP lane shifts; two
+// 64-block sub-tiles per wave): one source 81% against 78%, two 81% against
+// 76%, and 2-4 points more from four to sixteen sources.
+template <int N>
+__global__ __launch_bounds__(kRcUnalignedBlock) void rc_unaligned_kernel(ReduceArgs a) {
+    constexpr int BS = kRcUnalignedBlock;
+    const uint64_t nvec = a.nvec;
+    const uint64_t ntiles = (nvec + BS - 1) / BS;
+    const gf32x4u *src[N];
 #pragma unroll
-        for (int k = 0; k < N; k++) {
-            const uint32_t r = a.shift[k];
-            const uint64_t first = reinterpret_cast<uint64_t>(a.src[k] + a.head) - 4u * r + base * 16;
-            const uint32_t last = nblk - (r != 0 ? 0u : 1u);   // last block index covered
-            const gu32x4 *in = (const gu32x4 *)first;
+    for (int k = 0; k < N; k++)
+        src[k] = (const gf32x4u *)(a.src[k] + a.head);
+
+    for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const uint64_t base = t * BS;
+        const uint32_t nblk = (uint32_t)(nvec - base < (uint64_t)BS ? nvec - base : (uint64_t)BS);
+        if (threadIdx.x < nblk) {
+            const uint64_t i = base + threadIdx.x;
+            f32x4 val[N];
 #pragma unroll
-            for (int u = 0; u < U; u++) {
-                const uint32_t q = wbase + (uint32_t)u * 64u + lane;
-                xs[k][u] = __builtin_nontemporal_load(in + (q < last ? q : last));
-            }
-            const uint32_t qz = wbase + (uint32_t)(U * 64);
-            u32x4 z = {0u, 0u, 0u, 0u};
-            if (lane == 63)
-                z = __builtin_nontemporal_load(in + (qz < last ? qz : last));
-            zs[k] = z;
-        }
-        u32x4 ys[N][U];
+            for (int k = 0; k < N; k++)
+                val[k] = __builtin_nontemporal_load(src[k] + i);
+            f32x4 acc = val[0];
 #pragma unroll
-        for (int k = 0; k < N; k++)
-#pragma unroll
-            for (int u = 0; u < U; u++)
-                ys[k][u] = shl1_lane(xs[k][u], u + 1 < U ? rol1_lane(xs[k][u + 1 < U ? u + 1 : u]) : zs[k]);
-        const __amdgpu_buffer_rsrc_t out =
-            buffer_over(reinterpret_cast<uint64_t>(a.dst + a.head) + base * 16, nblk * 16u);
-#pragma unroll
-        for (int u = 0; u < U; u++) {
-            const uint32_t q = wbase + (uint32_t)u * 64u + lane;
-            if (q < nblk) {
-                f32x4 acc = rc_funnel(xs[0][u], ys[0][u], a.shift[0]);
-#pragma unroll
-                for (int k = 1; k < N; k++)
-                    acc = acc + rc_funnel(xs[k][u], ys[k][u], a.shift[k]);
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), out, q * 16, 0,
-                                                       kRcStorePol);
-            }
+            for (int k = 1; k < N; k++)
+                acc = acc + val[k];
+            const __amdgpu_buffer_rsrc_t out =
+                buffer_over(reinterpret_cast<uint64_t>(a.dst + a.head) + base * 16, nblk * 16u);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), out, threadIdx.x * 16, 0,
+                                                   kRcStorePol);
         }
     }
 
@@ -353,15 +276,14 @@ int reduce_grid(uint64_t nfloats, int nsrc, bool vector_path, int cu_count) {
     if (nsrc == 0)
         per_block = (uint64_t)kRcBlock * 4;
     else if (vector_path)
-        per_block = (uint64_t)rc_block_of(nsrc) * 4 * rc_unroll_of(nsrc);
+        per_block = (uint64_t)rc_block_of(nsrc) * 4;
     else
-        per_block = (uint64_t)rc_block_of(nsrc) * 4 * rc_shift_unroll_of(nsrc);
+        per_block = (uint64_t)kRcUnalignedBlock * 4;
     // one workgroup per tile, capped; the kernels loop when the cap binds
     uint64_t g = (nfloats + per_block - 1) / per_block;
-    g = (g + 7) & ~(uint64_t)7;            // a multiple of 8: keeps the XCD map
     if (g > kRcMaxBlocks)
         g = kRcMaxBlocks;
-    return (int)(g > 0 ? g : 8);
+    return (int)(g > 0 ? g : 1);
 }
 
 // Events the next launch made by this host thread records as part of the
@@ -394,7 +316,7 @@ template <int N>
 static hipError_t launch_n(const ReduceArgs &a, bool vector_path, int grid, hipStream_t s) {
     if (vector_path)
         return launch(rc_vec_kernel<N>, grid, rc_block_of(N), s, nullptr, a);
-    return launch(rc_shift_kernel<N>, grid, rc_block_of(N), s, nullptr, a);
+    return launch(rc_unaligned_kernel<N>, grid, kRcUnalignedBlock, s, nullptr, a);
 }
 
 hipError_t launch_reduce_copy(const ReduceArgs &a, int nsrc, bool vector_path, int cu_count,

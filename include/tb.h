@@ -158,9 +158,9 @@ int tb_prep_sources(float *dev_base, uint64_t slice_stride_bytes, uint64_t k,
  *              in exactly this order (subnormals kept).
  * dst: device pointer to nfloats floats; srcs: HOST array of nsrc device
  * pointers (read during the call only).  All pointers 4-byte aligned.  When
- * every source shares dst's address modulo 16 the sources are read as 16-byte
- * vectors directly; otherwise they are read as aligned 16-byte blocks and
- * realigned in registers (3-10 points of HBM peak slower at 256 MiB).
+ * every source shares dst's address modulo 16 the sources are read as aligned
+ * 16-byte vectors; otherwise each source is read with 16-byte loads at its own
+ * 4-byte alignment (3-7 points of HBM peak slower at 256 MiB).
  * dst may be exactly equal to a source; any other overlap between dst and a
  * source is rejected.  Enqueues one kernel on `stream`.  nfloats == 0 is a
  * no-op.

@@ -1,11 +1,14 @@
-"""Buffers above 4 GiB.  The reduce-copy kernels cap their grid at 2^20
-workgroups (4 GiB of 4 KiB tiles; 2 GiB of 2 KiB tiles per source from four
-sources up; 1 GiB of 1 KiB tiles above eight sources when some source
-disagrees with dst modulo 16) and loop over the tiles beyond it.  The
-oracle's definitions hold at any size and are checked as such: every byte of a
-memset is the memset byte, a one-source reduce-copy equals its source bitwise
-(both on the device), and a two-source sum equals the oracle's on sampled
-elements (TransferBench data validation, Expected destination)."""
+"""Buffers above the reduce-copy's grid cap and above 4 GiB.  The reduce-copy
+kernels cap their grid at 2^20 workgroups and loop over the tiles beyond it:
+the memset's 4 KiB tiles pass the cap above 4 GiB, the vector path's 1 KiB
+tiles (one or two sources) above 1 GiB per buffer and its 2 KiB tiles (three
+sources and more) above 2 GiB, and the unaligned path's 2 KiB tiles (any
+source count) above 2 GiB.  The oracle's
+definitions hold at any size and are checked as such: every byte of a memset
+is the memset byte and a one-source reduce-copy equals its source bitwise
+(both on the device), and every element of a multi-source sum equals the
+oracle's (TransferBench data validation, Expected destination), compared in
+contiguous chunks."""
 import numpy as np
 import pytest
 
@@ -57,62 +60,67 @@ def test_copy_above_4GiB_bitwise():
     assert _guards_on_device(dst)
 
 
-def test_reduce2_above_4GiB_sampled():
+CHUNK = 64 << 20                  # floats per comparison chunk (256 MiB per buffer)
+
+
+def _compare_all_chunks(torch, dst, srcs, n):
+    """Every element of dst against the oracle's fixed-order sum, 256 MiB of
+    each buffer at a time.  Chunks are read back as contiguous slices (plain
+    device-to-host copies): torch's advanced-index gather faulted on buffers
+    whose byte offsets pass 2^32, so no index kernel touches them."""
+    fd = _body(dst).view(torch.float32)
+    fs = [_body(b).view(torch.float32) for b in srcs]
+    for lo in range(0, n, CHUNK):
+        hi = min(lo + CHUNK, n)
+        got = fd[lo:hi].cpu().numpy()
+        exp = oracle.ref_reduce([f[lo:hi].cpu().numpy() for f in fs])
+        bad = oracle.first_mismatch(got, exp)
+        assert bad == -1, (f"element {lo + bad}: expected {exp[bad]!r} (0x{exp[bad:bad + 1].view(np.uint32)[0]:08x}), "
+                           f"got {got[bad]!r} (0x{got[bad:bad + 1].view(np.uint32)[0]:08x})")
+        del got, exp
+
+
+def _fill_finite(torch, buf, n, mul, add):
+    """Finite values, so the sum is the exact binary32 definition the oracle computes."""
+    i = torch.arange(n, dtype=torch.int64, device="cuda")
+    _body(buf).view(torch.float32).copy_(((i * mul + add) % 65521 - 32760).to(torch.float32) * 0.001)
+    del i
+
+
+def test_reduce2_above_4GiB_every_element():
     torch = require_gpu()
     import copy_reduce_amd as tb
-    note(f"max size: two-source sum n={N_BIG}, sampled against the oracle")
+    note(f"max size: two-source sum n={N_BIG}, every element against the oracle")
     a = DevBuf(torch, N_BIG * 4)
     b = DevBuf(torch, N_BIG * 4)
-    # finite values, so the sum is the exact binary32 definition the oracle computes
-    for buf, salt in ((a, 1), (b, 2)):
-        i = torch.arange(N_BIG, dtype=torch.int64, device="cuda")
-        _body(buf).view(torch.float32).copy_(((i * 40503 + salt) % 65521 - 32760).to(torch.float32) * 0.001)
-        del i
+    _fill_finite(torch, a, N_BIG, 40503, 1)
+    _fill_finite(torch, b, N_BIG, 40503, 2)
     dst = DevBuf(torch, N_BIG * 4, fill=0x11)
     tb.tb_reduce_copy(dst.ptr, [a.ptr, b.ptr], N_BIG, torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
-    # Samples are read back as contiguous slices (plain device-to-host copies):
-    # torch's advanced-index gather faulted on these buffers, whose byte
-    # offsets pass 2^32, so no index kernel touches them.
-    rng = np.random.default_rng(11)
-    starts = [0, N_BIG - 4096, (1 << 30) - 2048] + [int(x) for x in rng.integers(0, N_BIG - 1024, 64)]
-    fd, fa, fb = (_body(x).view(torch.float32) for x in (dst, a, b))
-    for lo in starts:
-        hi = min(lo + 4096, N_BIG)
-        got = fd[lo:hi].cpu().numpy()
-        exp = oracle.ref_reduce([fa[lo:hi].cpu().numpy(), fb[lo:hi].cpu().numpy()])
-        assert oracle.first_mismatch(got, exp) == -1, f"window at element {lo}"
+    _compare_all_chunks(torch, dst, [a, b], N_BIG)
     assert _guards_on_device(dst)
 
 
 @pytest.mark.parametrize("nsrc,n,offset,src_step", [
-    (5, (1 << 29) + 515, 8, 0),    # 2 GiB + 2,060 B per source: one-wave tiles past the grid cap
-    (3, (96 << 20) + 5, 4, 0),     # 384 MiB + 20 B per source: four-wave tiles, above the MALL size
-    (5, (1 << 29) + 261, 0, 4),    # 2 GiB + 1,044 B, sources 4/8/12/0/4 B off dst: realigning 2 KiB tiles past the cap
+    (5, (1 << 29) + 515, 8, 0),    # 2 GiB + 2,060 B per source: the vector path's 2 KiB tiles past the grid cap
+    (3, (96 << 20) + 5, 4, 0),     # 384 MiB + 20 B per source: above the memory-side cache's size
+    (2, (1 << 29) + 261, 0, 4),    # 2 GiB + 1,044 B, sources 4 / 8 B off dst: the unaligned path past the cap
+    (5, (1 << 29) + 261, 0, 4),    # the same with sources 4/8/12/0/4 B off
 ])
-def test_reduce_multi_source_large_sampled(nsrc, n, offset, src_step):
+def test_reduce_multi_source_large_every_element(nsrc, n, offset, src_step):
     torch = require_gpu()
     import copy_reduce_amd as tb
-    note(f"max size: {nsrc}-source sum n={n} offset {offset} source step {src_step}, sampled against the oracle")
+    note(f"max size: {nsrc}-source sum n={n} offset {offset} source step {src_step}, every element against the oracle")
     srcs = [DevBuf(torch, n * 4, offset=(offset + src_step * (k + 1)) % 16) for k in range(nsrc)]
     for k, buf in enumerate(srcs):
-        i = torch.arange(n, dtype=torch.int64, device="cuda")
-        _body(buf).view(torch.float32).copy_(((i * (40503 + 2 * k) + k) % 65521 - 32760).to(torch.float32) * 0.001)
-        del i
+        _fill_finite(torch, buf, n, 40503 + 2 * k, k)
     dst = DevBuf(torch, n * 4, offset=offset, fill=0x11)
     tb.tb_reduce_copy(dst.ptr, [b.ptr for b in srcs], n, torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(12 + nsrc)
-    starts = [0, n - 4096, (n // 2) & ~1023] + [int(x) for x in rng.integers(0, n - 1024, 48)]
-    fd = _body(dst).view(torch.float32)
-    fs = [_body(b).view(torch.float32) for b in srcs]
-    for lo in starts:
-        hi = min(lo + 4096, n)
-        got = fd[lo:hi].cpu().numpy()
-        exp = oracle.ref_reduce([f[lo:hi].cpu().numpy() for f in fs])
-        assert oracle.first_mismatch(got, exp) == -1, f"window at element {lo}"
+    _compare_all_chunks(torch, dst, srcs, n)
     assert _guards_on_device(dst)
-    del srcs, fs
+    del srcs
     torch.cuda.empty_cache()
 
 

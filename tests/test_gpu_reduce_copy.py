@@ -74,7 +74,7 @@ def test_reduce_copy_congruent_offsets_all_n(nsrc, off, n):
 @pytest.mark.parametrize("n", [7, 2053, 64 * 1024 + 3])
 def test_reduce_copy_mixed_offsets_all_n(nsrc, dst_off, n):
     """Source k at offset 4(k + 1) mod 16: sources that disagree with dst and
-    with each other modulo 16 (the realigning path; one source in four lines up
+    with each other modulo 16 (the unaligned path; one source in four lines up
     with dst when dst's offset is a multiple of 4 among them)."""
     torch = require_gpu()
     offs = [(4 * (k + 1)) % 16 for k in range(nsrc)]
@@ -84,21 +84,36 @@ def test_reduce_copy_mixed_offsets_all_n(nsrc, dst_off, n):
     assert dbuf.guards_intact()
 
 
-@pytest.mark.parametrize("nsrc", [1, 3, 4, 16])
-@pytest.mark.parametrize("body_blocks", [1, 63, 64, 65, 127, 128, 129, 511, 512, 513])
+@pytest.mark.parametrize("nsrc", [1, 2, 3, 4, 16])
+@pytest.mark.parametrize("body_blocks", [1, 63, 64, 65, 127, 128, 129, 255, 256, 257])
 @pytest.mark.parametrize("tail", [0, 3])
-def test_reduce_copy_realigning_subtile_edges(nsrc, body_blocks, tail):
-    """Realigning path with the float4 body ending on, just before and just
-    after the edges of a wave's two 64-block sub-tiles and of a tile (512
-    blocks for four-wave workgroups, 128 for one-wave ones), two tiles in:
-    the block after a sub-tile's lane 63 comes from the next sub-tile, the
-    next wave or lane 63's own load, each clamped at the body's end."""
+def test_reduce_copy_unaligned_tile_edges(nsrc, body_blocks, tail):
+    """Unaligned path (sources 4, 8, 12, 0 bytes off dst) with the float4 body
+    ending on, just before and just after the edges of a wave and of a
+    128-block tile, two tiles in: the last thread's 16-byte loads end exactly
+    at the sources' last body elements."""
     torch = require_gpu()
-    tile = 512 if nsrc <= 3 else 128
+    tile = 128
     n = 4 * (2 * tile + body_blocks) + tail
     offs = [(4 * (k + 1)) % 16 for k in range(nsrc)]
-    note(f"reduce_copy realigning nsrc={nsrc} n={n} source offsets {offs}")
+    note(f"reduce_copy unaligned nsrc={nsrc} n={n} source offsets {offs}")
     got, exp, dbuf, _ = _run(torch, _sources(nsrc, n, seed=body_blocks + tail), n, dst_off=0, src_offs=offs)
+    assert oracle.first_mismatch(got, exp) == -1
+    assert dbuf.guards_intact()
+
+
+@pytest.mark.parametrize("nsrc", [1, 2, 3, 4, 8, 16])
+@pytest.mark.parametrize("body_blocks", [1, 63, 64, 65, 127, 128, 129])
+def test_reduce_copy_vector_tile_edges(nsrc, body_blocks):
+    """Vector path with the float4 body ending at and around the edges of a
+    wave and of a tile (64 blocks up to two sources, 128 from three), two
+    tiles in, dst and sources 4 bytes past a 16-byte boundary (a head of three
+    floats) and a tail of two floats."""
+    torch = require_gpu()
+    tile = 64 if nsrc <= 2 else 128
+    n = 3 + 4 * (2 * tile + body_blocks) + 2
+    note(f"reduce_copy vector nsrc={nsrc} n={n} all offsets 4")
+    got, exp, dbuf, _ = _run(torch, _sources(nsrc, n, seed=body_blocks), n, dst_off=4, src_offs=[4] * nsrc)
     assert oracle.first_mismatch(got, exp) == -1
     assert dbuf.guards_intact()
 
@@ -137,7 +152,7 @@ def test_reduce_copy_memset_byte(mb):
 @pytest.mark.parametrize("nsrc,other_off", [(1, 0), (2, 0), (3, 0), (16, 0), (2, 4), (3, 8), (5, 12), (16, 4)])
 def test_reduce_copy_in_place_alias(nsrc, other_off):
     """dst == src0 exactly: every element is read before it is written.  With
-    the other sources off dst's alignment the realigning path runs, with the
+    the other sources off dst's alignment the unaligned path runs, with the
     aliased source at shift 0."""
     import copy_reduce_amd as tb
     torch = require_gpu()
