@@ -345,6 +345,12 @@ def main_line(args, torch, tb, wl):
     return line
 
 
+# ---------------------------------------------------------------------------
+# The oracle leg: the CPU oracle timed as the baseline, and the checks of the
+# GPU results against it.  These functions are the only place bench.py uses
+# oracle/ (the transfer path never does).
+# ---------------------------------------------------------------------------
+
 def cpu_baseline(torch, w, batch, dsts, pools):
     """The oracle, as it stands, timed on one host core over the full step,
     repeated for about CPU_BUDGET_S seconds (median); also checks the GPU
@@ -384,6 +390,38 @@ def cpu_baseline(torch, w, batch, dsts, pools):
         "cpu_model": _cpu_model(),
     }
     return cpu, validated
+
+
+def oracle_reduce_ok(dsts, w=None, srcs=None):
+    """Every element of each device view in dsts against the oracle's
+    fixed-order sum: of the workload's sources (oracle.gen_source) when w is
+    given, else of the device source views srcs, read back."""
+    import oracle
+    if w is not None:
+        host = [oracle.gen_source(w.nfloats, b, w.fill) for b in range(w.nsrc)]
+    else:
+        host = [x.cpu().numpy() for x in srcs]
+    exp = oracle.ref_reduce(host)
+    return all(oracle.first_mismatch(d.cpu().numpy(), exp) == -1 for d in dsts)
+
+
+def oracle_pool_ok(pools, batch, src_shift=0):
+    """Every byte of each pool (device uint8 views of at least batch.pool_bytes)
+    against the oracle's per-descriptor memcpy of the batch into an image
+    pre-filled with 0xA5.  src_shift: every descriptor read src_shift bytes
+    past its source offset, in the batch's source image followed by zero
+    bytes (as the misaligned study lays it out)."""
+    import numpy as np
+
+    import oracle
+    import workloads as wl
+    exp = np.full(batch.pool_bytes, wl.POOL_FILL, dtype=np.uint8)
+    image = np.zeros(batch.src_bytes + src_shift, dtype=np.uint8)
+    image[:batch.src_bytes] = batch.payload[:batch.src_bytes]
+    d = batch.desc.astype(np.uint64).copy()
+    d[:, 0] += np.uint64(src_shift)
+    oracle.ref_batch(exp, image, d)
+    return all(oracle.first_mismatch(p[:batch.pool_bytes].cpu().numpy(), exp) == -1 for p in pools)
 
 
 def cpu_baseline_suite(args, wl):
@@ -592,27 +630,6 @@ def percopy_submit(memcpy, srcs, dsts, sizes, kind, stream_handle):
     return time.perf_counter() - t0, rc
 
 
-def batch_sample_check(torch, pool, batch, src_dev):
-    """A consistency check of the harness (parity proper is the tests' and the
-    cpu_baseline leg's): every descriptor's first and last 16 bytes, and every
-    97th descriptor in full, equal their source bytes, compared on the device.
-    src_dev: a device uint8 tensor holding the batch's source image."""
-    import numpy as np
-    d = batch.desc.astype(np.int64)
-    d = d[d[:, 2] > 0]
-    k16 = np.minimum(np.arange(16)[None, :], d[:, 2][:, None] - 1)      # clipped to short copies
-    ends = np.concatenate([d[:, 1][:, None] + k16, (d[:, 1] + d[:, 2] - 1)[:, None] - k16], axis=1).ravel()
-    srcs = np.concatenate([d[:, 0][:, None] + k16, (d[:, 0] + d[:, 2] - 1)[:, None] - k16], axis=1).ravel()
-    dev = pool.device
-    if not torch.equal(pool[torch.from_numpy(ends).to(dev)], src_dev[torch.from_numpy(srcs).to(dev)]):
-        return False
-    for k in range(0, len(d), 97):
-        s0, d0, n0 = (int(x) for x in d[k])
-        if not torch.equal(pool[d0:d0 + n0], src_dev[s0:s0 + n0]):
-            return False
-    return True
-
-
 def baselines(args, torch, tb, wl):
     """The runtime's device-to-device copy (kernel, and copy engine) on the N = 1
     configurations, and one hipMemcpyAsync per descriptor for the batched ones:
@@ -643,7 +660,7 @@ def baselines(args, torch, tb, wl):
             ms, _, _ = timer.run([lambda i=i: one(i) for i in range(args.steps)])
             means.append((statistics.mean(ms), min(ms), max(ms)))
         med = sorted(means)[len(means) // 2]
-        ok = torch.equal(dst, rs.slice_view(0, 0))   # every slice holds the same data
+        ok = oracle_reduce_ok([dst], w)
         gbps = w.algorithmic_bytes / (med[0] * 1e-3) / 1e9
         out = {"config": w.name, "method": label, "k": rs.k, "reps": reps, "ms_mean": round(med[0], 5),
                "ms_min": round(med[1], 5), "ms_max": round(med[2], 5), "gbps": round(gbps, 1),
@@ -677,7 +694,7 @@ def baselines(args, torch, tb, wl):
                "wall_ms": round(wall * 1e3, 3), "host_submit_us_per_call": round(sub / batch.ncopies * 1e6, 3),
                "gbps": round(gbps, 2), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 5),
                "copies_per_s": round(batch.ncopies / wall, 1),
-               "validated_sample": batch_sample_check(torch, b["pool"], batch, b["src"])}
+               "validated": oracle_pool_ok([b["pool"]], batch)}
         del b
         torch.cuda.empty_cache()
         return out
@@ -737,11 +754,7 @@ def cache_study(args, torch, tb, wl):
                 flush()
                 ms, _, _ = timer.run([lambda p=rs.pointers(i): tb.tb_reduce_copy(dp, p, w.nfloats, sh)])
                 flushed.append(ms[0])
-            # consistency of the harness: one source is a bitwise copy, two are
-            # one binary32 addition (torch's, IEEE round to nearest even)
-            exp = rs.slice_view(0, 0) if nsrc == 1 else rs.slice_view(0, 0) + rs.slice_view(1, 0)
-            ok = torch.equal(dst, exp)
-            del exp
+            ok = oracle_reduce_ok([dst], w)
             wm, fm = statistics.mean(warm), statistics.mean(flushed)
             gb = w.algorithmic_bytes / 1e9
             print(json.dumps({"cache_study": {
@@ -756,55 +769,36 @@ def cache_study(args, torch, tb, wl):
 
 
 # ---------------------------------------------------------------------------
-# --interference: the batched copy beside a GEMM that fills the compute units
+# --interference: the batched copy beside a memory-bound neighbour
 # ---------------------------------------------------------------------------
 
 def interference(args, torch, tb, wl):
-    """A bf16 GEMM stream on a second stream (default priority) while C4 runs:
-    batched launches back to back for as long as the GEMMs run (uncapped, and
-    with the grid capped at 2,048 / 512 / 128 / 32 workgroups), and one
-    hipMemcpyAsync per descriptor; the slowdown of each side.  Mooncake RFC
-    #5041 (Motivation; Design of #5040, interference with compute) reports
-    per-call copies collapsing under such a GEMM and asks about CU budgets."""
-    import numpy as np
-
+    """The batched copy beside a memory-bound neighbour on a second stream
+    (default priority): torch's own copy of 512 MiB (1 GiB of HBM traffic per
+    kernel).  C4's batched launches run back to back for as long as 10
+    neighbour copies run, uncapped and with the grid capped at 512 and 32
+    workgroups (tb_batched_set_max_workgroups); the slowdown of each side.
+    Mooncake RFC #5041, Design of #5040: interference with other work, and its
+    open question on CU budgets."""
     s_copy = torch.cuda.current_stream()
-    s_gemm = torch.cuda.Stream()
+    s_other = torch.cuda.Stream()
     sh = s_copy.cuda_stream
     timer = Timed(torch, tb, s_copy)
-    M = 8192
-    g = torch.Generator(device="cuda").manual_seed(1)
-    A = torch.randn(M, M, dtype=torch.bfloat16, device="cuda", generator=g)
-    B = torch.randn(M, M, dtype=torch.bfloat16, device="cuda", generator=g)
-    C = torch.empty(M, M, dtype=torch.bfloat16, device="cuda")
-    flop = 2.0 * M ** 3
-
-    # a memory-bound neighbour: torch's own copy of 512 MiB (its kernel, not this library's)
     X = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     Y = torch.empty_like(X)
-    neighbour = {"gemm": lambda: torch.mm(A, B, out=C), "stream": lambda: Y.copy_(X)}
 
-    def gemms(n, kind="gemm"):
-        """Enqueue n GEMMs (or n neighbour copies) on the second stream between two events."""
+    def neighbours(n):
+        """n neighbour copies on the second stream between two events."""
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        op = neighbour[kind]
-        with torch.cuda.stream(s_gemm):
-            e0.record(s_gemm)
+        with torch.cuda.stream(s_other):
+            e0.record(s_other)
             for _ in range(n):
-                op()
-            e1.record(s_gemm)
+                Y.copy_(X)
+            e1.record(s_other)
         return e0, e1
 
-    with torch.cuda.stream(s_gemm):
-        for _ in range(3):
-            torch.mm(A, B, out=C)
-    torch.cuda.synchronize()
-    e0, e1 = gemms(10)
-    torch.cuda.synchronize()
-    gemm_ms = e0.elapsed_time(e1) / 10
-
     batch = wl.batch_c4()
-    b = setup_batch(torch, tb, batch, wl.DEFAULT_ROTATE_BYTES)
+    b = setup_batch(torch, tb, batch, wl.DEFAULT_ROTATE_BYTES, BATCH_DST_ROTATE_BYTES)
 
     def copies():
         for i in range(-args.warmup, 0):
@@ -813,90 +807,47 @@ def interference(args, torch, tb, wl):
         ms, _, _ = timer.run([lambda d=d: tb.tb_batched_copy(int(d.data_ptr()), batch.ncopies, sh) for d in ds])
         return statistics.mean(ms)
 
-    def overlap(cap, kind="gemm"):
-        """Batched copies back to back on the copy stream for as long as 10
-        neighbour kernels run on the other stream: both slowdowns against fresh
-        runs alone."""
+    def overlap(cap):
         tb.tb_batched_set_max_workgroups(cap)
         a_ms = copies()
-        gemms(3, kind)
-        e0, e1 = gemms(10, kind)
+        neighbours(3)
+        e0, e1 = neighbours(10)
         torch.cuda.synchronize()
-        g_alone = e0.elapsed_time(e1) / 10
-        m = int(1.2 * 10 * g_alone / a_ms) + 2
+        n_alone = e0.elapsed_time(e1) / 10
+        m = int(1.2 * 10 * n_alone / a_ms) + 2
         ds = [batch_desc_for(tb, b, i) for i in range(m)]
         c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        h0, h1 = gemms(10, kind)
+        h0, h1 = neighbours(10)
         c0.record(s_copy)
         for d in ds:
             tb.tb_batched_copy(int(d.data_ptr()), batch.ncopies, sh)
         c1.record(s_copy)
         torch.cuda.synchronize()
-        g_under = h0.elapsed_time(h1) / 10
+        n_under = h0.elapsed_time(h1) / 10
         c_window = c0.elapsed_time(c1)
         c_under = c_window / m
-        e0, e1 = gemms(10, kind)         # alone again after: the baseline is the faster of the two
+        e0, e1 = neighbours(10)          # alone again after: the baseline is the faster of the two
         torch.cuda.synchronize()
-        g_alone = min(g_alone, e0.elapsed_time(e1) / 10)
+        n_alone = min(n_alone, e0.elapsed_time(e1) / 10)
         return {"max_workgroups": cap or "none", "copies": m,
-                "us_alone": round(a_ms * 1e3, 2), "us_under_gemm": round(c_under * 1e3, 2),
+                "us_alone": round(a_ms * 1e3, 2), "us_beside_neighbour": round(c_under * 1e3, 2),
                 "copy_slowdown": round(c_under / a_ms, 3),
                 "gbps_alone": round(batch.algorithmic_bytes / (a_ms * 1e-3) / 1e9, 1),
-                "gbps_under_gemm": round(batch.algorithmic_bytes / (c_under * 1e-3) / 1e9, 1),
-                "neighbour_ms_alone": round(g_alone, 4), "neighbour_ms_beside_copies": round(g_under, 4),
-                "neighbour_slowdown": round(g_under / g_alone, 3),
-                "copy_window_over_gemm_window": round(c_window / (g_under * 10), 2),
-                "validated_sample": batch_sample_check(torch, b["pool"], batch, b["src"])}
+                "gbps_beside_neighbour": round(batch.algorithmic_bytes / (c_under * 1e-3) / 1e9, 1),
+                "neighbour_ms_alone": round(n_alone, 4), "neighbour_ms_beside_copies": round(n_under, 4),
+                "neighbour_slowdown": round(n_under / n_alone, 3),
+                "copy_window_over_neighbour_window": round(c_window / (n_under * 10), 2)}
 
-    runs, stream_runs = [], []
+    runs = []
     try:
-        for cap in (0, 2048, 512, 128, 32):
-            runs.append(overlap(cap))
         for cap in (0, 512, 32):
-            stream_runs.append(overlap(cap, "stream"))
+            runs.append(overlap(cap))
     finally:
         tb.tb_batched_set_max_workgroups(0)
-
-    # one hipMemcpyAsync per descriptor, the first 2,000 descriptors of C4
-    memcpy = hip_memcpy_fn()
-    k = 2000
-    pool_base = int(b["pool"].data_ptr())
-    srcs = (batch.desc[:k, 0].astype(np.int64) + b["base"]).tolist()
-    dsts = (batch.desc[:k, 1].astype(np.int64) + pool_base).tolist()
-    sizes = batch.desc[:k, 2].astype(np.int64).tolist()
-    bytes_k = 2 * int(batch.desc[:k, 2].sum())
-
-    def percopy():
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        _, rc = percopy_submit(memcpy, srcs, dsts, sizes, HIP_MEMCPY_D2D, sh)
-        s_copy.synchronize()
-        if rc != 0:
-            raise RuntimeError("hipMemcpyAsync failed")
-        return time.perf_counter() - t0
-
-    percopy()
-    pc_alone = statistics.median([percopy() for _ in range(3)])
-    ng2 = max(4, int(round(pc_alone * 1e3 * 3 / gemm_ms)) + 4)
-    g0, g1 = gemms(ng2)
-    pc_under = statistics.median([percopy() for _ in range(3)])
-    torch.cuda.synchronize()
-    sub = batch.desc[:k]
-    ok_percopy = all(torch.equal(b["pool"][int(d):int(d) + int(n)], b["src"][int(s):int(s) + int(n)])
-                     for s, d, n in sub[::50])
-    rec = {
-        "gemm": {"shape": [M, M, M], "dtype": "bf16", "ms_alone": round(gemm_ms, 4),
-                 "tflops_alone": round(flop / (gemm_ms * 1e-3) / 1e12, 1)},
-        "batched_copy_c4_beside_gemm": runs,
-        "batched_copy_c4_beside_stream_copy": {"neighbour": "torch copy_ of 512 MiB (1 GiB of HBM traffic per kernel)",
-                                               "runs": stream_runs},
-        "per_call_hipMemcpyAsync_2000_of_c4": {
-            "ms_alone": round(pc_alone * 1e3, 3), "ms_under_gemm": round(pc_under * 1e3, 3),
-            "slowdown": round(pc_under / pc_alone, 3),
-            "gbps_alone": round(bytes_k / pc_alone / 1e9, 3), "gbps_under_gemm": round(bytes_k / pc_under / 1e9, 3),
-            "validated_sample": ok_percopy},
-    }
+    rec = {"neighbour": "torch copy_ of 512 MiB (1 GiB of HBM traffic per kernel) on a second stream",
+           "batched_copy": "C4, 47,520 copies", "runs": runs,
+           "validated": oracle_pool_ok(pools_written(b, -args.warmup, args.steps), batch)}
     print(json.dumps({"interference": rec}), flush=True)
 
 
@@ -1022,10 +973,10 @@ def ring_study(args, torch, tb, wl):
                                                                        else "staged"),
                                                    "poll_ns": round(cached), "ctypes_floor_ns": round(floor)}}),
                   flush=True)
-        ok = batch_sample_check(torch, b["pool"], batch, b["src"])
-        print(json.dumps({"ring_validated_sample": {"batch": batch.name, "ok": ok}}), flush=True)
+        ok = oracle_pool_ok([b["pool"]], batch)
+        print(json.dumps({"ring_validated": {"batch": batch.name, "ok": ok}}), flush=True)
         if not ok:
-            raise RuntimeError(f"ring copies of {batch.name} differ from their sources")
+            raise RuntimeError(f"ring copies of {batch.name} differ from the oracle's")
         del b
         torch.cuda.empty_cache()
 
@@ -1035,51 +986,144 @@ def ring_study(args, torch, tb, wl):
 # ---------------------------------------------------------------------------
 
 def roofs(args, torch, tb, wl):
-    """Streams larger than the 256 MB memory-side cache: through the library,
-    a 1 GiB memset (nsrc = 0, writes only), a 16-source reduce of 64 MiB each
-    (reads 94% of the bytes) and a 512 MiB copy (half and half); for
-    reference, torch's own fill kernel over 1 GiB.  Then the launch floor:
-    per-launch times of a one-workgroup copy and of a 4 MiB copy, and the
-    host's cost of one tb_reduce_copy call for 1-16 sources."""
+    """What the access patterns allow, from instruments that share no code with
+    the library's kernels (libtb_roofs, include/tb_roofs.h; torch's own kernels
+    as an outside reference), each beside the library kernel that runs the same
+    pattern.  Every rate is the loop rate: the launches queued back to back
+    behind the spin gate, one event at each end, divided by the launch count.
+      1. streams larger than the 256 MB memory-side cache: read-only (the
+         instrument, and torch's sum), write-only (both store policies, the
+         library's memset, torch's fill) and a 512 MiB copy;
+      2. N + 1 streams of 64 MiB rotated over 4 slices read at once against
+         the reduce-copy with N sources (N reads, one write, destination
+         rotated the same way);
+      3. C4's 47,520 copies cut into <= 4 KiB tiles on the host (the same
+         bytes, source replicas and destination pools as the bench step): tile
+         copy, destinations written only, sources read only, against the
+         batched copy; the same for the copies packed side by side, and for
+         C5a's mixed batch.
+    Then the launch floor and the host's cost of one call."""
+    import numpy as np
+
+    import copy_reduce_amd.roofs as rf
+    import oracle
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
-    timer = Timed(torch, tb, stream)
     MiB = 1 << 20
     print(json.dumps({"roof_device": device_record(torch, tb)}), flush=True)
 
-    def timed(label, fn, nbytes, reads, writes):
-        for _ in range(args.warmup):
+    def loop_us(fns):
+        """Per-launch microseconds of fns (one per iteration, i = 0 .. steps-1)
+        run back to back after warmup launches of the same sequence."""
+        for fn in fns[:args.warmup]:
             fn()
-        ms, _, _ = timer.run([fn] * args.steps)
-        m = statistics.mean(ms)
-        gbps = nbytes / (m * 1e-3) / 1e9
-        print(json.dumps({"roof": {"stream": label, "bytes_read": reads, "bytes_written": writes,
-                                   "us_mean": round(m * 1e3, 2), "gbps": round(gbps, 1),
-                                   "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}}), flush=True)
+        ms, _ = run_whole(torch, tb, stream, fns)
+        return ms * 1e3 / len(fns)
 
+    def line(kind, label, us, nbytes, **extra):
+        gbps = nbytes / (us * 1e-6) / 1e9
+        rec = {"kind": kind, "stream": label, "bytes_per_launch": nbytes, "us_per_launch": round(us, 2),
+               "gbps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+        rec.update(extra)
+        print(json.dumps({"roof": rec}), flush=True)
+
+    # ---- 1. single streams above the memory-side cache's size ----
     big = torch.empty(256 * MiB, dtype=torch.float32, device="cuda")           # 1 GiB
-    bp = int(big.data_ptr())
-    timed("writes only: tb_reduce_copy nsrc=0, 1 GiB", lambda: tb.tb_reduce_copy(bp, [], big.numel(), sh, 0x5A),
-          1 << 30, 0, 1 << 30)
-    timed("writes only: torch fill_ (its own kernel), 1 GiB", lambda: big.view(torch.uint8).fill_(0x5A),
-          1 << 30, 0, 1 << 30)
-    srcs = [torch.full((16 * MiB,), float(k), dtype=torch.float32, device="cuda") for k in range(16)]   # 64 MiB each
-    dst = torch.empty(16 * MiB, dtype=torch.float32, device="cuda")
-    ptrs = [int(t.data_ptr()) for t in srcs]
-    dp = int(dst.data_ptr())
-    timed("reads 94%: tb_reduce_copy nsrc=16, 64 MiB each", lambda: tb.tb_reduce_copy(dp, ptrs, dst.numel(), sh),
-          17 * 64 * MiB, 16 * 64 * MiB, 64 * MiB)
-    del srcs, dst
-    a = big[:128 * MiB]
-    b = big[128 * MiB:]
-    ap, bp2 = int(a.data_ptr()), int(b.data_ptr())
-    timed("copy: tb_reduce_copy nsrc=1, 512 MiB", lambda: tb.tb_reduce_copy(bp2, [ap], a.numel(), sh),
-          1 << 30, 512 * MiB, 512 * MiB)
+    big2 = torch.empty_like(big)
+    bp, bp2 = int(big.data_ptr()), int(big2.data_ptr())
+    n = args.steps
+    line("instrument", "read-only, 1 GiB", loop_us([lambda: rf.tbr_read([bp], 1 << 30, sh)] * n), 1 << 30)
+    line("torch", "read-only: torch.sum over 1 GiB (its own reduction kernel)",
+         loop_us([lambda: big.sum()] * n), 1 << 30)
+    for pol, name in ((rf.TBR_STORE_STREAMING, "nt sc0 sc1"), (rf.TBR_STORE_DEVICE, "sc1")):
+        line("instrument", f"write-only, 1 GiB, {name} stores",
+             loop_us([lambda pol=pol: rf.tbr_write([bp], 1 << 30, 0x3F800000, pol, sh)] * n), 1 << 30)
+    line("library", "write-only: tb_reduce_copy nsrc=0, 1 GiB",
+         loop_us([lambda: tb.tb_reduce_copy(bp, [], big.numel(), sh, 0x5A)] * n), 1 << 30)
+    line("torch", "write-only: torch fill_ over 1 GiB (its own kernel)",
+         loop_us([lambda: big.view(torch.uint8).fill_(0x5A)] * n), 1 << 30)
+    half = 512 * MiB
+    for pol, name in ((rf.TBR_STORE_STREAMING, "nt sc0 sc1"), (rf.TBR_STORE_DEVICE, "sc1")):
+        line("instrument", f"copy 512 MiB, {name} stores, destination alternating between two buffers",
+             loop_us([lambda i=i, pol=pol: rf.tbr_copy(bp2 + (i % 2) * half, bp, half, pol, sh)
+                      for i in range(n)]), 2 * half)
+    line("library", "copy 512 MiB: tb_reduce_copy nsrc=1, destination alternating between two buffers",
+         loop_us([lambda i=i: tb.tb_reduce_copy(bp2 + (i % 2) * half, [bp], half // 4, sh) for i in range(n)]),
+         2 * half)
+    del big, big2
+    torch.cuda.empty_cache()
+
+    # ---- 2. N + 1 read streams against the N-source reduce-copy ----
+    nb, kslices = 64 * MiB, 4
+    bufs = [torch.empty(kslices * nb, dtype=torch.uint8, device="cuda") for _ in range(17)]
+    for t in bufs:
+        t.fill_(0x3C)
+    dsts = torch.empty(kslices * nb, dtype=torch.uint8, device="cuda")
+    base = [int(t.data_ptr()) for t in bufs]
+    dbase = int(dsts.data_ptr())
+    for nsrc in (1, 2, 4, 8, 16):
+        k = nsrc + 1
+        line("instrument", f"read-only, {k} streams of 64 MiB rotated over 4 slices",
+             loop_us([lambda i=i, k=k: rf.tbr_read([b + (i % kslices) * nb for b in base[:k]], nb, sh)
+                      for i in range(n)]), k * nb, streams=k)
+        line("library", f"tb_reduce_copy nsrc={nsrc}, 64 MiB per buffer, sources and destination rotated over 4 "
+             "slices", loop_us([lambda i=i, nsrc=nsrc: tb.tb_reduce_copy(
+                 dbase + (i % kslices) * nb, [b + (i % kslices) * nb for b in base[:nsrc]], nb // 4, sh)
+                 for i in range(n)]), (nsrc + 1) * nb, nsrc=nsrc)
+    del bufs, dsts
+    torch.cuda.empty_cache()
+
+    # ---- 3. C4's pattern: the same bytes as host-cut tiles against the batched copy ----
+    for placement, label, batch in (("random_slots", "C4 random_slots", wl.batch_c4_placed("random_slots")),
+                                    ("packed", "C4 packed", wl.batch_c4_placed("packed")),
+                                    ("c5a", "C5a", wl.batch_c5())):
+        b = setup_batch(torch, tb, batch, wl.DEFAULT_ROTATE_BYTES, BATCH_DST_ROTATE_BYTES)
+        tiles = {}
+        for (sbase, pbase) in b["descs"]:
+            t = rf.cut_tiles(batch.desc, sbase, pbase)
+            tiles[(sbase, pbase)] = torch.from_numpy(t.view(np.int64)).cuda()
+        ntiles = next(iter(tiles.values())).shape[0]
+
+        def tiles_for(i):
+            (src,) = tb.tb_rotate_sources([b["base"]], b["stride"], b["kb"], i)
+            (pool,) = tb.tb_rotate_sources([b["pbase"]], b["pstride"], b["kp"], i)
+            return int(tiles[(src, pool)].data_ptr())
+        payload = batch.algorithmic_bytes
+        extra = {"placement": placement, "copies": batch.ncopies, "tiles": ntiles, "replicas": b["kb"],
+                 "pools": b["kp"]}
+        line("library", f"{label}: tb_batched_copy",
+             loop_us([lambda d=batch_desc_for(tb, b, i): tb.tb_batched_copy(int(d.data_ptr()), batch.ncopies, sh)
+                      for i in range(n)]), payload, **extra)
+        for pol, name in ((rf.TBR_STORE_STREAMING, "nt sc0 sc1"), (rf.TBR_STORE_DEVICE, "sc1")):
+            line("instrument", f"{label}: tile copy, {name} stores",
+                 loop_us([lambda i=i, pol=pol: rf.tbr_tiles_copy(tiles_for(i), ntiles, pol, sh)
+                          for i in range(n)]), payload, **extra)
+        line("instrument", f"{label}: destinations written only, nt sc0 sc1 stores",
+             loop_us([lambda i=i: rf.tbr_tiles_write(tiles_for(i), ntiles, 0xA5A5A5A5, rf.TBR_STORE_STREAMING, sh)
+                      for i in range(n)]), payload // 2, **extra)
+        line("instrument", f"{label}: sources read only",
+             loop_us([lambda i=i: rf.tbr_tiles_read(tiles_for(i), ntiles, sh) for i in range(n)]),
+             payload // 2, **extra)
+        # the tile copy writes the batch's bytes: check one pool against the oracle
+        b["pool_views"][0].fill_(wl.POOL_FILL)
+        rf.tbr_tiles_copy(tiles_for(0), ntiles, rf.TBR_STORE_STREAMING, sh)
+        torch.cuda.synchronize()
+        exp = np.full(batch.pool_bytes, wl.POOL_FILL, dtype=np.uint8)
+        oracle.ref_batch(exp, batch.payload, batch.desc)
+        ok = oracle.first_mismatch(b["pool_views"][0].cpu().numpy(), exp) == -1
+        print(json.dumps({"roof_check": {"placement": placement, "tile_copy_equals_oracle": ok}}), flush=True)
+        if not ok:
+            raise RuntimeError(f"the tile copy of {label} differs from the oracle")
+        del b, tiles, exp
+        torch.cuda.empty_cache()
 
     # Launch floor: a copy of 64 floats (one workgroup, next to no work) and
     # C1's 4 MiB copy, 20 launches back to back (one event at each end) and by
     # each launch's own start and stop events.
     n1 = 1 << 20
+    floor_buf = torch.empty(9 * n1, dtype=torch.float32, device="cuda")      # 8 sources of 4 MiB + dst
+    ap = int(floor_buf.data_ptr())
+    bp2 = ap + 8 * 4 * n1
     for label, nf in (("copy of 256 B (one workgroup)", 64), ("copy of 4 MiB (C1 size)", n1)):
         fns = [lambda j=j, nf=nf: tb.tb_reduce_copy(bp2, [ap + (j % 8) * 4 * n1], nf, sh) for j in range(20)]
         for fn in fns[:args.warmup]:
@@ -1146,7 +1190,7 @@ def scatter_study(args, torch, tb, wl):
             "kernel_us": round(km * 1e3, 2), "kernel_frac_of_peak": round(nbytes / (km * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "loop_us_per_launch": round(lm * 1e3, 2),
             "loop_frac_of_peak": round(nbytes / (lm * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-            "validated_sample": batch_sample_check(torch, b["pool"], batch, b["src"])}}), flush=True)
+            "validated": oracle_pool_ok([b["pool"]], batch)}}), flush=True)
         del b
         torch.cuda.empty_cache()
 
@@ -1157,8 +1201,8 @@ def misaligned_study(args, torch, tb, wl):
     sources, every source 0, 4 or 8 bytes past a 16-byte boundary while dst
     sits on one.  Then the batched copy over C4's copies with every source
     shifted by 0, 1, 2, 4 or 8 bytes.  Kernel time from the launches' own events, mean of 10 after
-    3 warmups; the result is checked against torch's own binary32 additions in
-    the same order."""
+    3 warmups; every result is checked against the oracle (every element of dst,
+    every byte of the pool)."""
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     n = 64 << 20
@@ -1176,11 +1220,7 @@ def misaligned_study(args, torch, tb, wl):
                 fns[0]()
             ms, _ = run_launch_events(torch, tb, stream, fns)
             m = statistics.mean(ms)
-            ref = srcs[0][k:k + n].clone()
-            for x in srcs[1:]:
-                ref += x[k:k + n]
-            ok = torch.equal(dst[:n], ref)
-            del ref
+            ok = oracle_reduce_ok([dst[:n]], srcs=[x[k:k + n] for x in srcs])
             print(json.dumps({"misaligned": {
                 "nsrc": nsrc, "bytes_per_buffer": n * 4, "source_offset_bytes": off_bytes,
                 "path": "vector" if off_bytes == 0 else "realigning",
@@ -1207,13 +1247,11 @@ def misaligned_study(args, torch, tb, wl):
             fns[0]()
         ms, _ = run_launch_events(torch, tb, stream, fns)
         m = statistics.mean(ms)
-        rng = np.random.default_rng(shift)
-        ok = all(torch.equal(pool[int(d[i, 1]):int(d[i, 1] + d[i, 2])], src[int(d[i, 0]):int(d[i, 0] + d[i, 2])])
-                 for i in rng.integers(0, batch.ncopies, 500))
+        ok = oracle_pool_ok([pool], batch, src_shift=shift)
         print(json.dumps({"misaligned_batch": {
             "copies": batch.ncopies, "source_shift_bytes": shift, "kernel_us": round(m * 1e3, 2),
             "frac_of_peak": round(batch.algorithmic_bytes / (m * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-            "validated_sample_500": ok}}), flush=True)
+            "validated": ok}}), flush=True)
 
 
 def calibrate_copy(torch, tb):
@@ -1240,7 +1278,8 @@ def main():
                     help="only time the HIP runtime's own copies (copy kernel, copy engine, one call per "
                          "descriptor) on the same inputs, then exit")
     ap.add_argument("--interference", action="store_true",
-                    help="only time C4 (batched, and one call per descriptor) alone and beside a bf16 GEMM, then exit")
+                    help="only time C4's batched copy alone and beside a memory-bound neighbour (torch's 512 MiB "
+                         "copy on a second stream), uncapped and with its grid capped, then exit")
     ap.add_argument("--cpu-suite", action="store_true",
                     help="only time the oracle on one host core for every configuration (no GPU), then exit")
     ap.add_argument("--ring", action="store_true",

@@ -18,6 +18,9 @@ LIB = os.path.join(PKG, "libtb.so")
 ARCH = "gfx950"
 
 SOURCES = ["tb_host.cpp", "tb_gen.cpp", "tb_ring.cpp", "tb_kernels.hip"]
+# The measuring instruments of bench.py --roofs: a library of their own.
+ROOFS_SOURCES = ["tb_roofs.hip"]
+ROOFS_LIB = os.path.join(PKG, "libtb_roofs.so")
 
 COMMON = [
     "-std=c++17", "-O3", "-fPIC", "-Wall", "-Wextra", "-Werror",
@@ -49,19 +52,26 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link copy_reduce_amd/libtb.so (always rebuilds)."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"link of libtb.so failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"link of {os.path.basename(lib)} failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source for gfx950 and link copy_reduce_amd/libtb.so and
+    copy_reduce_amd/libtb_roofs.so (always rebuilds)."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + ROOFS_SOURCES
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in SOURCES], LIB, verbose)
+    _link([objs[s] for s in ROOFS_SOURCES], ROOFS_LIB, verbose)
     return LIB
 
 

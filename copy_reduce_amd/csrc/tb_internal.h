@@ -15,8 +15,9 @@ namespace tbk {
 // vector paths up to three sources (from four sources up they run one-wave
 // workgroups).
 constexpr int kRcBlock = 256;
-// Grid cap of the reduce-copy (a multiple of 8); below it every tile has its
-// own workgroup.
+// Grid cap of the reduce-copy (a multiple of 64, so a workgroup's XCD and its
+// place in a group of 64 stay fixed across the grid-stride loop); below it
+// every tile has its own workgroup.
 constexpr uint64_t kRcMaxBlocks = 1u << 20;
 
 struct ReduceArgs {

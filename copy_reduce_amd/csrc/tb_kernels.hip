@@ -199,6 +199,30 @@ typedef __attribute__((address_space(1))) f32x4u gf32x4u;
 // 16-byte blocks and realigned them in registers (DPP lane shifts; two
 // 64-block sub-tiles per wave): one source 81% against 78%, two 81% against
 // 76%, and 2-4 points more from four to sixteen sources.
+//
+// For one or two sources, tiles are dealt in blocks of eight per XCD:
+// workgroup b runs on XCD b mod 8, and within every 64 consecutive
+// workgroups XCD x takes the eight consecutive tiles 8x .. 8x + 7, so the
+// 128-byte lines that straddle two tiles are mostly read by one XCD's L2
+// while the chip still works on one compact window.  Measured with sources 4
+// bytes off dst: two sources 83% against 81% in plain order, a copy 81.3%
+// against 80.7%; eight sources alike, sixteen 1 point slower, and every
+// aligned case 2-5 points slower, so it is used here only.
+template <int N>
+constexpr bool rc_unaligned_map() {
+    return N <= 2;
+}
+
+// Tile of workgroup b under that deal: a bijection on [0, ntiles) that
+// permutes each complete group of 64 and leaves the last, partial group in
+// order (gridDim.x is the whole grid or the cap, a multiple of 64, so b mod 8
+// stays the XCD across the grid-stride loop).
+__device__ __forceinline__ uint64_t xcd_block_tile(uint64_t b, uint64_t ntiles) {
+    if ((b | 63u) >= ntiles)
+        return b;
+    return (b & ~(uint64_t)63) + (b & 7) * 8 + ((b >> 3) & 7);
+}
+
 template <int N>
 __global__ __launch_bounds__(kRcUnalignedBlock) void rc_unaligned_kernel(ReduceArgs a) {
     constexpr int BS = kRcUnalignedBlock;
@@ -209,7 +233,8 @@ __global__ __launch_bounds__(kRcUnalignedBlock) void rc_unaligned_kernel(ReduceA
     for (int k = 0; k < N; k++)
         src[k] = (const gf32x4u *)(a.src[k] + a.head);
 
-    for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    for (uint64_t b = blockIdx.x; b < ntiles; b += gridDim.x) {
+        const uint64_t t = rc_unaligned_map<N>() ? xcd_block_tile(b, ntiles) : b;
         const uint64_t base = t * BS;
         const uint32_t nblk = (uint32_t)(nvec - base < (uint64_t)BS ? nvec - base : (uint64_t)BS);
         if (threadIdx.x < nblk) {

@@ -1,7 +1,8 @@
 """CPU oracle for the transfer hot path -- TEST INFRASTRUCTURE ONLY.
 
-Only tests/, __graft_entry__.smoke() and the cpu_baseline leg of bench.py may
-import this package.  It wraps oracle/liboracle.so (plain single-threaded C,
+Only tests/, __graft_entry__.smoke() and the oracle leg of bench.py (the CPU
+baseline and the checks of the benchmark's GPU results) may import this
+package.  It wraps oracle/liboracle.so (plain single-threaded C,
 see oracle.c for the page and section each function follows) with numpy
 arrays.  It never imports the HIP package and the HIP package never imports it.
 """
@@ -45,6 +46,9 @@ def _load():
     lib.orc_ref_batch.argtypes = [_vp, _vp, _vp, _u64]
     lib.orc_first_mismatch.restype = _i64
     lib.orc_first_mismatch.argtypes = [_vp, _vp, _u64, _u64]
+    lib.orc_mismatch_report.restype = ctypes.c_int
+    lib.orc_mismatch_report.argtypes = [_vp, _vp, _u64, _u64, ctypes.POINTER(_i64), ctypes.POINTER(_u64),
+                                        ctypes.POINTER(_u64)]
     lib.orc_time_ref_reduce.restype = ctypes.c_double
     lib.orc_time_ref_reduce.argtypes = [_vp, _vp, ctypes.c_int, _u64, ctypes.c_uint]
     lib.orc_time_ref_batch.restype = ctypes.c_double
@@ -150,6 +154,34 @@ def first_mismatch(out: np.ndarray, expected: np.ndarray) -> int:
     b = np.ascontiguousarray(expected)
     assert a.nbytes == b.nbytes and a.itemsize == b.itemsize
     return int(_lib.orc_first_mismatch(_ptr(a), _ptr(b), a.nbytes, a.itemsize))
+
+
+def mismatch_report(out: np.ndarray, expected: np.ndarray):
+    """None if byte-identical, else (index, expected, actual) of the first
+    differing element, the values in the arrays' dtype ("TransferBench data
+    validation", How validation works: a failure names the first differing
+    element with its expected and actual values)."""
+    a = np.ascontiguousarray(out)
+    b = np.ascontiguousarray(expected)
+    assert a.nbytes == b.nbytes and a.itemsize == b.itemsize and 1 <= a.itemsize <= 8
+    idx, eb, ab = _i64(), _u64(), _u64()
+    if not _lib.orc_mismatch_report(_ptr(a), _ptr(b), a.nbytes, a.itemsize, ctypes.byref(idx), ctypes.byref(eb),
+                                    ctypes.byref(ab)):
+        return None
+    as_dtype = lambda bits: np.frombuffer(int(bits).to_bytes(8, "little")[:a.itemsize], dtype=a.dtype)[0]
+    return int(idx.value), as_dtype(eb.value), as_dtype(ab.value)
+
+
+def assert_equal(out: np.ndarray, expected: np.ndarray, what: str = "") -> None:
+    """Raise AssertionError naming the first differing element, its expected
+    and its actual value (with their bits), unless the arrays are identical."""
+    rep = mismatch_report(out, expected)
+    if rep is None:
+        return
+    i, e, a = rep
+    bits = lambda v: "0x" + np.asarray(v).tobytes()[::-1].hex()
+    raise AssertionError(f"{what + ': ' if what else ''}first difference at element {i}: "
+                         f"expected {e.item()!r} ({bits(e)}), got {a.item()!r} ({bits(a)})")
 
 
 def time_ref_reduce(srcs, n: int = None, memset_byte: int = 0):

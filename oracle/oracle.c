@@ -2,8 +2,8 @@
  * oracle.c -- CPU oracle for the transfer hot path.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path loads, links or calls
- * this file: only the test suite, the smoke check and the CPU-baseline leg of
- * the benchmark do.  It shares no code, header, table or helper with the HIP
+ * this file: only the test suite, the smoke check and the oracle leg of the
+ * benchmark (its CPU baseline and the checks of its GPU results) do.  It shares no code, header, table or helper with the HIP
  * library (copy_reduce_amd/), and it includes no HIP header.
  *
  * Everything here is written to be checked by eye against the pages:
@@ -262,6 +262,28 @@ int64_t orc_first_mismatch(const void *out, const void *expected,
         if (a[i] != b[i])
             return (int64_t)(i / elem_size);
     return -1;
+}
+
+/*
+ * The same validation with the report the page describes for a failure: the
+ * first differing element's index together with its expected and actual
+ * values (here their bytes, as the low elem_size bytes of a little-endian
+ * 64-bit word; elem_size is 1 .. 8).  Returns 0 when the buffers are equal
+ * (the outputs are left untouched), else 1.
+ */
+int orc_mismatch_report(const void *out, const void *expected, uint64_t nbytes, uint64_t elem_size,
+                        int64_t *index, uint64_t *expected_bits, uint64_t *actual_bits)
+{
+    const int64_t i = orc_first_mismatch(out, expected, nbytes, elem_size);
+    if (i < 0)
+        return 0;
+    uint64_t e = 0, a = 0;
+    memcpy(&e, (const unsigned char *)expected + (uint64_t)i * elem_size, (size_t)elem_size);
+    memcpy(&a, (const unsigned char *)out + (uint64_t)i * elem_size, (size_t)elem_size);
+    *index = i;
+    *expected_bits = e;
+    *actual_bits = a;
+    return 1;
 }
 
 /* ------------------------------------------------------------------------ */

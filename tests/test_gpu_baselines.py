@@ -30,7 +30,7 @@ def test_runtime_copy_of_rotated_slices(kind):
         (p,) = rs.pointers(i)
         assert memcpy(int(dst.data_ptr()), p, n * 4, getattr(bench, kind), sh) == 0
     torch.cuda.synchronize()
-    assert oracle.first_mismatch(dst.cpu().numpy(), oracle.gen_source(n, 0, None)) == -1
+    oracle.assert_equal(dst.cpu().numpy(), oracle.gen_source(n, 0, None))
 
 
 @pytest.mark.parametrize("kind", KINDS)
@@ -51,8 +51,8 @@ def test_one_call_per_descriptor(kind):
     assert rc == 0
     exp = np.full(b.pool_bytes, wl.POOL_FILL, dtype=np.uint8)
     oracle.ref_batch(exp, b.payload, b.desc)
-    assert oracle.first_mismatch(pool.cpu().numpy(), exp) == -1
-    assert bench.batch_sample_check(torch, pool, b, src)
+    oracle.assert_equal(pool.cpu().numpy(), exp)
+    assert bench.oracle_pool_ok([pool], b)
     k = int(np.flatnonzero(b.desc[:, 2] > 0)[0])
     pool[int(b.desc[k, 1])] ^= 0xFF        # one flipped byte must be caught
-    assert not bench.batch_sample_check(torch, pool, b, src)
+    assert not bench.oracle_pool_ok([pool], b)

@@ -37,10 +37,12 @@ def _run_batch(torch, batch: wl.Batch, src_shift: int = 0, dst_shift: int = 0, s
     d[:, 0] += np.uint64(src_shift)
     d[:, 1] += np.uint64(dst_shift)
     oracle.ref_batch(exp, image, d)
-    first = oracle.first_mismatch(got, exp)
-    if first != -1:
-        _describe_mismatch(got, exp, d)
-    return first
+    rep = oracle.mismatch_report(got, exp)
+    if rep is None:
+        return -1
+    note(f"  first differing byte {rep[0]}: expected {int(rep[1]):#04x}, got {int(rep[2]):#04x}")
+    _describe_mismatch(got, exp, d)
+    return rep[0]
 
 
 def _describe_mismatch(got, exp, desc):
@@ -344,7 +346,7 @@ def test_refused_under_graph_capture():
     got = pool.cpu().numpy()
     exp = np.full(b.pool_bytes, wl.POOL_FILL, dtype=np.uint8)
     oracle.ref_batch(exp, b.payload, b.desc)
-    assert oracle.first_mismatch(got, exp) == -1
+    oracle.assert_equal(got, exp)
 
 
 def test_threads_on_their_own_streams():
@@ -384,7 +386,7 @@ def test_threads_on_their_own_streams():
     for b, _, pool, _, _ in jobs:
         exp = np.full(b.pool_bytes, wl.POOL_FILL, dtype=np.uint8)
         oracle.ref_batch(exp, b.payload, b.desc)
-        assert oracle.first_mismatch(pool.cpu().numpy(), exp) == -1
+        oracle.assert_equal(pool.cpu().numpy(), exp)
 
 
 @pytest.mark.parametrize("cap", [8, 64, 1000])
@@ -416,7 +418,7 @@ def test_workgroup_cap_gives_identical_bytes(cap):
         tb.tb_batched_set_max_workgroups(0)
     exp = np.full(b.pool_bytes, wl.POOL_FILL, dtype=np.uint8)
     oracle.ref_batch(exp, b.payload, b.desc)
-    assert oracle.first_mismatch(pool.cpu().numpy(), exp) == -1
+    oracle.assert_equal(pool.cpu().numpy(), exp)
 
 
 def test_threads_sharing_one_stream():
@@ -459,7 +461,7 @@ def test_threads_sharing_one_stream():
     for b, _, pool, _ in jobs:
         exp = np.full(b.pool_bytes, wl.POOL_FILL, dtype=np.uint8)
         oracle.ref_batch(exp, b.payload, b.desc)
-        assert oracle.first_mismatch(pool.cpu().numpy(), exp) == -1
+        oracle.assert_equal(pool.cpu().numpy(), exp)
 
 
 def _random_mixed_batch(seed):

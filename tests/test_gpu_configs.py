@@ -26,9 +26,9 @@ def _reduce_config(torch, w: wl.ReduceWorkload, always_validate: bool):
         tb.tb_reduce_copy(int(dst.data_ptr()), rs.pointers(i), w.nfloats, stream)
         if always_validate and i >= 0:
             torch.cuda.synchronize()
-            assert oracle.first_mismatch(dst.cpu().numpy(), exp) == -1, f"iteration {i}"
+            oracle.assert_equal(dst.cpu().numpy(), exp, f"iteration {i}")
     torch.cuda.synchronize()
-    assert oracle.first_mismatch(dst.cpu().numpy(), exp) == -1
+    oracle.assert_equal(dst.cpu().numpy(), exp)
 
 
 @pytest.mark.parametrize("name,always", [("c1_copy_4MiB_rot", True), ("c2_reduce2_256MiB_rot", False),
@@ -70,7 +70,7 @@ def _batch_config(torch, batch: wl.Batch, replicas: int):
     del pool, src
     exp = np.full(batch.pool_bytes, wl.POOL_FILL, dtype=np.uint8)
     oracle.ref_batch(exp, batch.payload, batch.desc)
-    assert oracle.first_mismatch(got, exp) == -1
+    oracle.assert_equal(got, exp)
 
 
 @pytest.mark.parametrize("which", ["c4", "c5"])

@@ -74,9 +74,7 @@ def _compare_all_chunks(torch, dst, srcs, n):
         hi = min(lo + CHUNK, n)
         got = fd[lo:hi].cpu().numpy()
         exp = oracle.ref_reduce([f[lo:hi].cpu().numpy() for f in fs])
-        bad = oracle.first_mismatch(got, exp)
-        assert bad == -1, (f"element {lo + bad}: expected {exp[bad]!r} (0x{exp[bad:bad + 1].view(np.uint32)[0]:08x}), "
-                           f"got {got[bad]!r} (0x{got[bad:bad + 1].view(np.uint32)[0]:08x})")
+        oracle.assert_equal(got, exp, f"chunk at element {lo}")
         del got, exp
 
 
@@ -160,7 +158,7 @@ def test_batched_copy_millions_of_descriptors():
     torch.cuda.synchronize()
     exp = np.full(pool_bytes, wl.POOL_FILL, dtype=np.uint8)
     oracle.ref_batch(exp, batch.payload, desc)
-    assert oracle.first_mismatch(pool.cpu().numpy(), exp) == -1
+    oracle.assert_equal(pool.cpu().numpy(), exp)
 
 
 def test_batched_copy_of_one_copy_above_4GiB():

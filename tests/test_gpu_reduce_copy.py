@@ -42,7 +42,7 @@ def test_reduce_copy_all_n_ragged(nsrc, n):
     note(f"reduce_copy nsrc={nsrc} n={n} compress seed=3")
     srcs = _sources(nsrc, n)
     got, exp, dbuf, _ = _run(torch, srcs, n)
-    assert oracle.first_mismatch(got, exp) == -1
+    oracle.assert_equal(got, exp)
     assert dbuf.guards_intact()
 
 
@@ -52,7 +52,7 @@ def test_reduce_copy_pointer_offsets_n2(offs):
     n = 4096 + 13
     note(f"reduce_copy nsrc=2 n={n} offsets={offs}")
     got, exp, dbuf, _ = _run(torch, _sources(2, n), n, dst_off=offs[0], src_offs=list(offs[1:]))
-    assert oracle.first_mismatch(got, exp) == -1
+    oracle.assert_equal(got, exp)
     assert dbuf.guards_intact()
 
 
@@ -65,7 +65,7 @@ def test_reduce_copy_congruent_offsets_all_n(nsrc, off, n):
     torch = require_gpu()
     note(f"reduce_copy nsrc={nsrc} n={n} all offsets {off}")
     got, exp, dbuf, _ = _run(torch, _sources(nsrc, n, seed=nsrc), n, dst_off=off, src_offs=[off] * nsrc)
-    assert oracle.first_mismatch(got, exp) == -1
+    oracle.assert_equal(got, exp)
     assert dbuf.guards_intact()
 
 
@@ -80,7 +80,7 @@ def test_reduce_copy_mixed_offsets_all_n(nsrc, dst_off, n):
     offs = [(4 * (k + 1)) % 16 for k in range(nsrc)]
     note(f"reduce_copy nsrc={nsrc} n={n} dst offset {dst_off} source offsets {offs}")
     got, exp, dbuf, _ = _run(torch, _sources(nsrc, n, seed=nsrc + 100), n, dst_off=dst_off, src_offs=offs)
-    assert oracle.first_mismatch(got, exp) == -1
+    oracle.assert_equal(got, exp)
     assert dbuf.guards_intact()
 
 
@@ -98,7 +98,7 @@ def test_reduce_copy_unaligned_tile_edges(nsrc, body_blocks, tail):
     offs = [(4 * (k + 1)) % 16 for k in range(nsrc)]
     note(f"reduce_copy unaligned nsrc={nsrc} n={n} source offsets {offs}")
     got, exp, dbuf, _ = _run(torch, _sources(nsrc, n, seed=body_blocks + tail), n, dst_off=0, src_offs=offs)
-    assert oracle.first_mismatch(got, exp) == -1
+    oracle.assert_equal(got, exp)
     assert dbuf.guards_intact()
 
 
@@ -114,7 +114,7 @@ def test_reduce_copy_vector_tile_edges(nsrc, body_blocks):
     n = 3 + 4 * (2 * tile + body_blocks) + 2
     note(f"reduce_copy vector nsrc={nsrc} n={n} all offsets 4")
     got, exp, dbuf, _ = _run(torch, _sources(nsrc, n, seed=body_blocks), n, dst_off=4, src_offs=[4] * nsrc)
-    assert oracle.first_mismatch(got, exp) == -1
+    oracle.assert_equal(got, exp)
     assert dbuf.guards_intact()
 
 
@@ -127,7 +127,7 @@ def test_reduce_copy_pointer_offsets_random(seed):
     offs = [int(x) * 4 for x in rng.integers(0, 4, size=nsrc + 1)]
     note(f"reduce_copy nsrc={nsrc} n={n} offsets={offs}")
     got, exp, dbuf, _ = _run(torch, _sources(nsrc, n, seed=seed), n, dst_off=offs[0], src_offs=offs[1:])
-    assert oracle.first_mismatch(got, exp) == -1
+    oracle.assert_equal(got, exp)
     assert dbuf.guards_intact()
 
 
@@ -137,7 +137,7 @@ def test_reduce_copy_default_pattern_large(nsrc):
     n = (1 << 22) + 3
     note(f"reduce_copy nsrc={nsrc} n={n} default pattern")
     got, exp, _, _ = _run(torch, _sources(nsrc, n, "default"), n)
-    assert oracle.first_mismatch(got, exp) == -1
+    oracle.assert_equal(got, exp)
 
 
 @pytest.mark.parametrize("mb", [0x00, 0x5A, 0xFF])
@@ -146,7 +146,8 @@ def test_reduce_copy_memset_byte(mb):
     n = 100003
     note(f"reduce_copy nsrc=0 n={n} memset={mb:#x}")
     got, exp, dbuf, _ = _run(torch, [], n, dst_off=4, memset_byte=mb, prefill=0x11)
-    assert oracle.first_mismatch(got, exp) == -1 and dbuf.guards_intact()
+    oracle.assert_equal(got, exp)
+    assert dbuf.guards_intact()
 
 
 @pytest.mark.parametrize("nsrc,other_off", [(1, 0), (2, 0), (3, 0), (16, 0), (2, 4), (3, 8), (5, 12), (16, 4)])
@@ -162,7 +163,7 @@ def test_reduce_copy_in_place_alias(nsrc, other_off):
     bufs = [DevBuf(torch, n * 4, offset=0 if k == 0 else other_off).upload(s) for k, s in enumerate(srcs)]
     tb.tb_reduce_copy(bufs[0].ptr, [b.ptr for b in bufs], n, torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
-    assert oracle.first_mismatch(bufs[0].download().view(np.float32), oracle.ref_reduce(srcs)) == -1
+    oracle.assert_equal(bufs[0].download().view(np.float32), oracle.ref_reduce(srcs))
 
 
 def test_torch_api_rejects_strided_tensors():
@@ -229,7 +230,7 @@ def test_prep_sources_replicates_slices():
             ref = oracle.gen_compress(nfloats, b, wl.C3_PCT, 3)
             for s in range(rs.k):
                 got = rs.slice_view(b, s).cpu().numpy()
-                assert oracle.first_mismatch(got, ref) == -1, (b, s)
+                oracle.assert_equal(got, ref, str((b, s)))
 
 
 def test_rotation_selects_slice_i_mod_k():
@@ -256,7 +257,7 @@ def test_rotation_selects_slice_i_mod_k():
         torch.cuda.synchronize()
         s = oracle.slice_of(i, k)
         exp = oracle.ref_reduce([oracle.gen_default(nfloats, s + 16 * b) for b in range(nsrc)])
-        assert oracle.first_mismatch(dst.cpu().numpy(), exp) == -1, i
+        oracle.assert_equal(dst.cpu().numpy(), exp, str(i))
 
 
 def test_reduce_copy_on_side_stream():
@@ -271,7 +272,7 @@ def test_reduce_copy_on_side_stream():
     torch.cuda.synchronize()
     tb.tb_reduce_copy(dst.ptr, [b.ptr for b in bufs], n, side.cuda_stream)
     side.synchronize()
-    assert oracle.first_mismatch(dst.download().view(np.float32), oracle.ref_reduce(srcs)) == -1
+    oracle.assert_equal(dst.download().view(np.float32), oracle.ref_reduce(srcs))
 
 
 def test_reduce_copy_invalid_args_enqueue_nothing():
@@ -313,7 +314,7 @@ def test_reduce_copy_captured_in_a_graph_replays_exactly(nsrc):
         g.replay()
         torch.cuda.synchronize()
         got = dbuf.download().view(np.float32)
-        assert oracle.first_mismatch(got, exp) == -1, f"replay {rep}"
+        oracle.assert_equal(got, exp, f"replay {rep}")
         assert dbuf.guards_intact()
 
 

@@ -34,13 +34,15 @@ class _Dev:
         self.host_desc = d
         torch.cuda.synchronize()
 
-    def first_mismatch(self) -> int:
+    def check(self) -> None:
+        """The pool against the oracle's, byte for byte (a failure names the
+        first differing byte with its expected and actual value)."""
         b = self.batch
         exp = np.full(b.pool_bytes + 64, wl.POOL_FILL, dtype=np.uint8)
         image = np.zeros(b.src_bytes + 64, dtype=np.uint8)
         image[:b.src_bytes] = b.payload[:b.src_bytes]
         oracle.ref_batch(exp, image, b.desc)
-        return oracle.first_mismatch(self.pool.cpu().numpy(), exp)
+        oracle.assert_equal(self.pool.cpu().numpy(), exp, "pool")
 
 
 def _requests(n: int, rng, most: int):
@@ -76,7 +78,7 @@ def test_random_requests_through_small_ring(direct, seed):
         tickets = _submit_all(ring, dev.host_desc, cuts)
         ring.wait(tickets[-1])
         assert all(ring.poll(t) for t in tickets)
-    assert dev.first_mismatch() == -1
+    dev.check()
 
 
 @pytest.mark.parametrize("direct", [False, True], ids=["staged", "direct"])
@@ -105,7 +107,7 @@ def test_lengths_1B_to_3MiB_one_request_each(direct):
         tickets = _submit_all(ring, dev.host_desc, [(i, i + 1) for i in range(n)])
         assert tickets == list(range(1, n + 1))
         ring.wait(tickets[-1])
-    assert dev.first_mismatch() == -1
+    dev.check()
 
 
 @pytest.mark.parametrize("direct", [False, True], ids=["staged", "direct"])
@@ -121,7 +123,7 @@ def test_mixed_kv_batch_in_page_sized_requests(direct):
     with DescRing(direct=direct) as ring:
         tickets = _submit_all(ring, dev.host_desc, cuts)
         ring.wait(tickets[-1])
-    assert dev.first_mismatch() == -1
+    dev.check()
 
 
 def test_tickets_poll_wait_and_empty_submits():
@@ -146,7 +148,7 @@ def test_tickets_poll_wait_and_empty_submits():
             ring.wait(4)
         ring.wait(t2)
         assert ring.poll(1) and ring.poll(2) and ring.poll(3)
-    assert dev.first_mismatch() == -1
+    dev.check()
 
 
 def test_bad_descriptor_rejects_whole_request():
@@ -175,7 +177,7 @@ def test_bad_descriptor_rejects_whole_request():
     exp_batch = wl.Batch(b.name, np.concatenate([[[0, 0, 0]], b.desc[1:]]).astype(np.uint64), b.src_bytes,
                          b.pool_bytes, b.seed, payload=b.payload)
     dev.batch = exp_batch
-    assert dev.first_mismatch() == -1
+    dev.check()
 
 
 @pytest.mark.parametrize("direct", [False, True], ids=["staged", "direct"])
@@ -189,7 +191,7 @@ def test_destroy_waits_for_work_in_flight(direct):
     for a in range(0, b.ncopies, 1000):
         ring.submit(dev.host_desc[a:a + 1000])
     ring.close()                     # no wait before: destroy must wait itself
-    assert dev.first_mismatch() == -1
+    dev.check()
 
 
 @pytest.mark.parametrize("mode", ["no_wait", "no_pieces"])
@@ -209,7 +211,7 @@ def test_recovery_modes_through_ring(mode):
             ring.wait(t)
     finally:
         tb.tb_batched_set_mode(tb.TB_BC_NORMAL)
-    assert dev.first_mismatch() == -1
+    dev.check()
 
 
 @pytest.mark.parametrize("direct", [False, True], ids=["staged", "direct"])
@@ -234,7 +236,7 @@ def test_ring_and_plain_calls_interleave_on_one_stream(direct):
                 t = ring.submit(dev.host_desc[a:a + m])
         ring.wait(t)
         s.synchronize()
-    assert dev.first_mismatch() == -1
+    dev.check()
 
 
 def test_two_rings_from_two_threads():
@@ -267,4 +269,4 @@ def test_two_rings_from_two_threads():
     assert not errors, errors
     torch.cuda.synchronize()
     for dev in devs:
-        assert dev.first_mismatch() == -1
+        dev.check()

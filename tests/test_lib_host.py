@@ -107,13 +107,13 @@ def _lib_gen(n, b, fill):
 @pytest.mark.parametrize("n", [1, 15, 16, 17, 383, 384, 1000, 16 * 4096 + 7])
 @pytest.mark.parametrize("b", [0, 1, 3, 15])
 def test_prep_reference_default_equals_oracle(n, b):
-    assert oracle.first_mismatch(_lib_gen(n, b, None), oracle.gen_default(n, b)) == -1
+    oracle.assert_equal(_lib_gen(n, b, None), oracle.gen_default(n, b))
 
 
 def test_prep_reference_default_large_index():
     # indices past 2^24 (the 256 MiB buffers reach 2^26)
     n = (1 << 24) + 1000
-    assert oracle.first_mismatch(_lib_gen(n, 1, None), oracle.gen_default(n, 1)) == -1
+    oracle.assert_equal(_lib_gen(n, 1, None), oracle.gen_default(n, 1))
 
 
 @pytest.mark.parametrize("n", [1, 15, 16, 17, 1000, 65536 + 3])
@@ -122,21 +122,21 @@ def test_prep_reference_default_large_index():
                                       ((0, 0, 0, 0, 100), 77), ((20, 20, 20, 20, 20), 2**63 + 5)])
 def test_prep_reference_compress_equals_oracle(n, b, pct, seed):
     got = _lib_gen(n, b, ("compress", pct, seed))
-    assert oracle.first_mismatch(got, oracle.gen_compress(n, b, pct, seed)) == -1
+    oracle.assert_equal(got, oracle.gen_compress(n, b, pct, seed))
 
 
 def test_prep_reference_compress_c3_buffers_equal_oracle():
     n = 16 << 20
     for b in range(4):
         got = _lib_gen(n, b, ("compress", wl.C3_PCT, wl.C3_SEED))
-        assert oracle.first_mismatch(got, oracle.gen_compress(n, b, wl.C3_PCT, wl.C3_SEED)) == -1
+        oracle.assert_equal(got, oracle.gen_compress(n, b, wl.C3_PCT, wl.C3_SEED))
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 10, 1001])
 def test_prep_reference_pattern_equals_oracle(n):
     pat = np.array([1.0, -0.0, 3.5e-40, float("inf"), 2.5], dtype=np.float32)
     got = _lib_gen(n, 4, ("pattern", pat))
-    assert oracle.first_mismatch(got, oracle.gen_pattern(n, pat)) == -1
+    oracle.assert_equal(got, oracle.gen_pattern(n, pat))
 
 
 def test_prep_reference_rejects_bad_config():

@@ -188,7 +188,7 @@ def test_reduce_default_pattern_closed_form(nsrc):
     srcs = [oracle.gen_default(n, b) for b in range(nsrc)]
     v = oracle.gen_default(n, 0).astype(np.int64)
     expected = (v * (nsrc * (nsrc + 1) // 2)).astype(np.float32)
-    assert oracle.first_mismatch(oracle.ref_reduce(srcs), expected) == -1
+    oracle.assert_equal(oracle.ref_reduce(srcs), expected)
 
 
 def test_reduce_zero_sources_is_memset():
@@ -216,7 +216,7 @@ def test_reduce_each_step_correctly_rounded():
     for k in range(2, 5):
         cur = oracle.ref_reduce(srcs[:k])
         exact = prev.astype(np.float64) + srcs[k - 1].astype(np.float64)
-        assert oracle.first_mismatch(cur, exact.astype(np.float32)) == -1
+        oracle.assert_equal(cur, exact.astype(np.float32))
         prev = cur
 
 
@@ -340,10 +340,31 @@ def test_c4_placements_keep_the_copies_and_move_only_destinations():
 # --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("where", [0, 12345, 99999])
+def test_mismatch_report_names_index_expected_and_actual(where):
+    """A failure names the first differing element with its expected and
+    actual values: a planted float and a planted byte are reported exactly."""
+    exp = oracle.gen_default(100000, 1)
+    assert oracle.mismatch_report(exp.copy(), exp) is None
+    out = exp.copy()
+    out[where] = np.float32(-0.375)
+    if where + 7 < out.size:
+        out[where + 7] = np.float32(1e30)                 # a later difference is not the one reported
+    i, e, a = oracle.mismatch_report(out, exp)
+    assert (i, e.view(np.uint32), a.view(np.uint32)) == (where, exp[where].view(np.uint32),
+                                                        np.float32(-0.375).view(np.uint32))
+    with pytest.raises(AssertionError, match=f"element {where}: expected {float(exp[where])!r} .* got -0.375"):
+        oracle.assert_equal(out, exp)
+    pool = np.full(4096, 0xA5, np.uint8)
+    bad = pool.copy()
+    bad[where % 4096] = 0x3C
+    assert oracle.mismatch_report(bad, pool) == (where % 4096, 0xA5, 0x3C)
+
+
+@pytest.mark.parametrize("where", [0, 12345, 99999])
 def test_first_mismatch_reports_corrupted_index(where):
     exp = oracle.gen_default(100000, 0)
     out = exp.copy()
-    assert oracle.first_mismatch(out, exp) == -1
+    oracle.assert_equal(out, exp)
     out.view(np.uint8)[where * 4 + 2] ^= 0x40
     assert oracle.first_mismatch(out, exp) == where
     bout, bexp = out.view(np.uint8), exp.view(np.uint8)

@@ -47,9 +47,8 @@ def _pools(torch, batch: wl.Batch, src_shift: int = 0, dst_shift: int = 0):
 def _check(torch, batch, label, **kw):
     note(f"no-alloc batched copy: {label} ({batch.ncopies} copies, {batch.total_bytes} B)")
     ref, got, exp = _pools(torch, batch, **kw)
-    assert oracle.first_mismatch(ref, exp) == -1, f"{label}: tb_batched_copy differs from the oracle"
-    bad = oracle.first_mismatch(got, ref)
-    assert bad == -1, f"{label}: tb_batched_copy_noalloc differs from tb_batched_copy at byte {bad}"
+    oracle.assert_equal(ref, exp, f"{label}: tb_batched_copy differs from the oracle")
+    oracle.assert_equal(got, ref, f"{label}: tb_batched_copy_noalloc against tb_batched_copy")
 
 
 def test_noalloc_matches_batched_copy_twice_smaller_second():
