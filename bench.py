@@ -1197,7 +1197,7 @@ def scatter_study(args, torch, tb, wl):
 
 def misaligned_study(args, torch, tb, wl):
     """The reduce-copy when its sources disagree with dst modulo 16 (the
-    realigning path) against aligned sources: 256 MiB per buffer, 1-16
+    unaligned path) against aligned sources: 256 MiB per buffer, 1-16
     sources, every source 0, 4 or 8 bytes past a 16-byte boundary while dst
     sits on one.  Then the batched copy over C4's copies with every source
     shifted by 0, 1, 2, 4 or 8 bytes.  Kernel time from the launches' own events, mean of 10 after
@@ -1223,7 +1223,7 @@ def misaligned_study(args, torch, tb, wl):
             ok = oracle_reduce_ok([dst[:n]], srcs=[x[k:k + n] for x in srcs])
             print(json.dumps({"misaligned": {
                 "nsrc": nsrc, "bytes_per_buffer": n * 4, "source_offset_bytes": off_bytes,
-                "path": "vector" if off_bytes == 0 else "realigning",
+                "path": "vector" if off_bytes == 0 else "unaligned",
                 "kernel_us": round(m * 1e3, 2),
                 "frac_of_peak": round((nsrc + 1) * n * 4 / (m * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "validated": ok}}),
                   flush=True)

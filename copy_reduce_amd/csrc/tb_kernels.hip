@@ -77,18 +77,23 @@ constexpr bool rc_buffer_loads(int nsrc) { return nsrc >= 2 && nsrc <= 8; }
 // workgroups.
 constexpr int kRcUnalignedBlock = 128;
 
-// Sources are streamed once per launch: nontemporal loads (without them the
-// kernel measured 73% of peak instead of 92%).  Results are written with
-// nontemporal system-scope stores (nt sc0 sc1), which do not allocate in the
+// Sources are streamed once per launch: nontemporal loads (without them, or
+// with device-scope loads, two sources of 256 MiB ran at 77% instead of 85%).
+// Results are written with nontemporal stores, which do not allocate in the
 // 256 MB memory-side cache (MALL): the kernel's rate is then the same whether
 // or not the destination was written recently.  Device-scope stores (sc1)
 // allocate there, and a fixed destination rewritten launch after launch (the
 // pages' timing) then reads 92-93% for two sources of 256 MiB, against 81-82%
-// once the destination rotates over 1 GiB, where these stores reach 84-85%
-// under either timing.  Stores that allocate in the MALL also leave dirty
-// lines that a following kernel pays for: behind such batched-copy stores the
-// next 256 MiB reduce-copy fell from 81% to 67%.
-constexpr int kRcStorePol = kPolNt | kPolSc0 | kPolSc1;
+// once the destination rotates over 1 GiB, where nontemporal stores reach
+// 84-85% under either timing.  Stores that allocate in the MALL also leave
+// dirty lines that a following kernel pays for: behind such batched-copy
+// stores the next 256 MiB reduce-copy fell from 81% to 67%.  Up to two
+// sources the stores also carry system scope (nt sc0 sc1: written through the
+// per-XCD L2): a 512 MiB copy 84.3% against 82.8% with nt alone, and the
+// bench's two-source step 85.1% against 84.5%.  From three sources up nt
+// alone is faster: four sources of 64 MiB 82-83% against 79-81%, the same
+// with a rotated destination (no cache help either way).
+constexpr int rc_store_pol(int nsrc) { return nsrc <= 2 ? (kPolNt | kPolSc0 | kPolSc1) : kPolNt; }
 __device__ __forceinline__ f32x4 rc_load(const gf32x4 *p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ float rc_load(const gf32 *p) { return __builtin_nontemporal_load(p); }
 
@@ -140,7 +145,7 @@ __global__ __launch_bounds__(rc_block_of(N)) void rc_vec_kernel(ReduceArgs a) {
             const __amdgpu_buffer_rsrc_t out =
                 buffer_over(reinterpret_cast<uint64_t>(a.dst + a.head) + base * 16, nblk * 16u);
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), out, threadIdx.x * 16, 0,
-                                                   kRcStorePol);
+                                                   rc_store_pol(N));
         }
     }
 
@@ -250,7 +255,7 @@ __global__ __launch_bounds__(kRcUnalignedBlock) void rc_unaligned_kernel(ReduceA
             const __amdgpu_buffer_rsrc_t out =
                 buffer_over(reinterpret_cast<uint64_t>(a.dst + a.head) + base * 16, nblk * 16u);
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), out, threadIdx.x * 16, 0,
-                                                   kRcStorePol);
+                                                   rc_store_pol(N));
         }
     }
 
@@ -271,8 +276,10 @@ __global__ __launch_bounds__(kRcUnalignedBlock) void rc_unaligned_kernel(ReduceA
 
 // nsrc == 0: dstReference[0] is a memset.  dst is 4-byte aligned; `fill` is
 // the memset byte replicated into 32 bits.  One 4 KiB tile per workgroup and
-// one 16-byte store per thread: on MI355X this shape writes at 86% of HBM
-// peak, where four stores per thread (16 KiB per workgroup) reach only 75%.
+// one 16-byte store per thread: on MI355X this shape writes 1 GiB at 89-90%
+// of HBM peak, where four stores per thread (16 KiB per workgroup) reach only
+// 75%.  Stores as for one or two sources (nt sc0 sc1, not allocating in the
+// memory-side cache).
 __global__ __launch_bounds__(kRcBlock) void rc_memset_kernel(ReduceArgs a) {
     const uint64_t nvec = a.nvec;
     const u32x4 fill4 = {a.fill, a.fill, a.fill, a.fill};
@@ -284,7 +291,7 @@ __global__ __launch_bounds__(kRcBlock) void rc_memset_kernel(ReduceArgs a) {
         const __amdgpu_buffer_rsrc_t out =
             buffer_over(reinterpret_cast<uint64_t>(a.dst + a.head) + base * 16, (uint32_t)(n16 * 16));
         if (threadIdx.x < n16)
-            __builtin_amdgcn_raw_buffer_store_b128(fill4, out, threadIdx.x * 16, 0, kPolSc1);
+            __builtin_amdgcn_raw_buffer_store_b128(fill4, out, threadIdx.x * 16, 0, rc_store_pol(0));
     }
     if (blockIdx.x == 0) {
         gu32 *d32 = (gu32 *)(a.dst);
@@ -323,18 +330,25 @@ void set_next_launch_events(hipEvent_t start, hipEvent_t stop) {
 
 // Every kernel of the library is launched here.  With events (the timing hook,
 // or `done` from the caller), the launch carries them as its own start / stop
-// events, so no separate event command sits between kernels.
+// events, so no separate event command sits between kernels.  A launch has
+// one stop event: when `done` takes it (a ring slot's completion event) and
+// the timing hook also set one, the hook's is recorded right after the launch
+// as a command of its own, so it too fires when the kernel has completed.
 template <typename... KArgs, typename... Args>
 static hipError_t launch(void (*kernel)(KArgs...), int grid, int block, hipStream_t s, hipEvent_t done,
                          Args... args) {
     const hipEvent_t start = t_next_start;
-    const hipEvent_t stop = done != nullptr ? done : t_next_stop;
+    const hipEvent_t hook_stop = t_next_stop;
+    const hipEvent_t stop = done != nullptr ? done : hook_stop;
     t_next_start = t_next_stop = nullptr;
     if (start != nullptr || stop != nullptr)
         hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(block), 0, s, start, stop, 0u, args...);
     else
         hipLaunchKernelGGL(kernel, dim3(grid), dim3(block), 0, s, args...);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && done != nullptr && hook_stop != nullptr)
+        e = hipEventRecord(hook_stop, s);
+    return e;
 }
 
 template <int N>

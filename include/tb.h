@@ -329,8 +329,11 @@ int tb_ring_destroy(tb_ring *ring);
  * launch (hipExtLaunchKernel's launch events) instead of being separate
  * commands between kernels, which on MI355X add about 3 us per launch to a
  * back-to-back sequence.  Either event may be NULL (a hipEvent_t created by
- * the caller, with timing enabled to read elapsed times).  One launch only;
- * a call that fails before launching leaves the hook set for the next.
+ * the caller, with timing enabled to read elapsed times).  A ring launch's
+ * own stop event is its slot's completion event: the hook's stop event is
+ * then recorded by a separate command right after that launch (it still
+ * fires when the kernel has completed).  One launch only; a call that fails
+ * before launching leaves the hook set for the next.
  * Always TB_OK.
  */
 int tb_time_next_launch(void *start_event, void *stop_event);

@@ -270,3 +270,31 @@ def test_two_rings_from_two_threads():
     torch.cuda.synchronize()
     for dev in devs:
         dev.check()
+
+
+@pytest.mark.parametrize("direct", [False, True], ids=["staged", "direct"])
+def test_timing_hook_on_a_ring_launch(direct):
+    """tb_time_next_launch before a ring submit: the launch records the start
+    event and its slot's completion event, and the hook's stop event is
+    recorded after it too (it is not dropped)."""
+    torch = require_gpu()
+    from copy_reduce_amd.torch_api import DescRing
+    b = wl.batch_c4(seed=9, n=3000, pool_bytes=64 << 20)
+    dev = _Dev(torch, b)
+    s = torch.cuda.current_stream()
+    st, sp, ref = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    st.record(s)
+    sp.record(s)
+    ref.record(s)                                 # later than both first records
+    torch.cuda.synchronize()
+    note(f"ring timing hook direct={direct}")
+    with DescRing(nslots=2, slot_descs=4096, direct=direct, stream=s) as ring:
+        import copy_reduce_amd as tb
+        tb.tb_time_next_launch(st.cuda_event, sp.cuda_event)
+        t = ring.submit(dev.host_desc)
+        ring.wait(t)
+        torch.cuda.synchronize()
+    assert ref.elapsed_time(st) > 0.0             # recorded again, by the launch
+    assert ref.elapsed_time(sp) > ref.elapsed_time(st)
+    assert 0.0 < st.elapsed_time(sp) < 50.0
+    dev.check()
