@@ -11,9 +11,8 @@ namespace tbk {
 
 // ---- reduce-copy -----------------------------------------------------------
 
-// Workgroup size of the reduce-copy kernels (4 wave64s): the memset, and the
-// vector paths up to three sources (from four sources up they run one-wave
-// workgroups).
+// Workgroup size of the reduce-copy's memset (N = 0): 4 wave64s, one 4 KiB
+// tile.  The summing kernels size their workgroups by source count.
 constexpr int kRcBlock = 256;
 // Grid cap of the reduce-copy (a multiple of 64, so a workgroup's XCD and its
 // place in a group of 64 stay fixed across the grid-stride loop); below it

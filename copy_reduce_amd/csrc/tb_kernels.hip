@@ -31,6 +31,8 @@ typedef __attribute__((address_space(1))) float gf32;
 typedef __attribute__((address_space(1))) u32x4 gu32x4;
 typedef __attribute__((address_space(1))) uint32_t gu32;
 typedef __attribute__((address_space(1))) uint8_t gu8;
+typedef __attribute__((address_space(1))) void gvoid;
+typedef __attribute__((address_space(3))) void svoid;
 
 // Cache-policy bits of gfx950 buffer instructions (the aux operand): nt marks
 // the line for early eviction (streaming); sc0 / sc1 set the coherence scope
@@ -76,6 +78,13 @@ constexpr bool rc_buffer_loads(int nsrc) { return nsrc >= 2 && nsrc <= 8; }
 // copy and two sources of 256 MiB against 79% and 76% with one-wave
 // workgroups.
 constexpr int kRcUnalignedBlock = 128;
+// From eight sources up the unaligned path stages every source's aligned
+// 16-byte blocks in LDS and reads each thread's four floats back at the
+// source's own 4-byte offset (rc_unaligned_lds_kernel): one-wave workgroups,
+// all eight sources staged at once at N = 8, four at a time above.
+constexpr bool rc_unaligned_lds(int nsrc) { return nsrc >= 8; }
+constexpr int kRcLdsBlock = 64;
+constexpr int rc_lds_group(int nsrc) { return nsrc <= 8 ? nsrc : 4; }
 
 // Sources are streamed once per launch: nontemporal loads (without them, or
 // with device-scope loads, two sources of 256 MiB ran at 77% instead of 85%).
@@ -194,8 +203,8 @@ __device__ __forceinline__ u32x4 rol1_lane(u32x4 x) {
 typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
 typedef __attribute__((address_space(1))) f32x4u gf32x4u;
 
-// Unaligned path: every pointer is 4-byte aligned and some source disagrees
-// with dst modulo 16.  dst is cut as on the vector path (head floats, float4
+// Unaligned path up to seven sources: every pointer is 4-byte aligned and
+// some source disagrees with dst modulo 16.  dst is cut as on the vector path (head floats, float4
 // body, tail floats); the thread that writes dst body block i reads, from
 // every source, the 16 bytes holding that source's four elements for it, with
 // one 16-byte load at the elements' own (4-byte) alignment.  Every load reads
@@ -205,19 +214,20 @@ typedef __attribute__((address_space(1))) f32x4u gf32x4u;
 // 64-block sub-tiles per wave): one source 81% against 78%, two 81% against
 // 76%, and 2-4 points more from four to sixteen sources.
 //
-// For one or two sources, tiles are dealt in blocks of eight per XCD:
-// workgroup b runs on XCD b mod 8, and within every 64 consecutive
-// workgroups XCD x takes the eight consecutive tiles 8x .. 8x + 7, so the
-// 128-byte lines that straddle two tiles are mostly read by one XCD's L2
-// while the chip still works on one compact window.  Measured with sources 4
-// bytes off dst: two sources 83% against 81% in plain order, a copy 81.3%
-// against 80.7%; eight sources alike, sixteen 1 point slower, and every
-// aligned case 2-5 points slower, so it is used here only.
-template <int N>
-constexpr bool rc_unaligned_map() {
-    return N <= 2;
-}
-
+// Tiles are dealt in blocks of eight per XCD: workgroup b runs on XCD b mod 8,
+// and within every 64 consecutive workgroups XCD x takes the eight
+// consecutive tiles 8x .. 8x + 7, so the 128-byte line that straddles two
+// tiles of a source is mostly read by one XCD's L2 while the chip still works
+// on one compact window.  In plain order neighbouring tiles run on different
+// XCDs and both fetch that line from HBM: with four to sixteen sources 4
+// bytes off dst, 6.6-7.7% more bytes read than the sources hold (one or two
+// sources, dealt: 0.8-0.9%).  Measured at 256 MiB per buffer, sources 4 or 8
+// bytes off dst: four sources 78.7-79.4% of HBM peak against 75.9-76.3% in
+// plain order, eight 72.5-72.8% against 71.2-71.7%, sixteen 69.9-70.5%
+// against 69.5-70.0%; two sources 83% against 81%.  Blocks of sixteen tiles
+// per XCD gained nothing more.  (On the vector path, with buffers on line
+// boundaries so that no tiles share a line, the same deal cost 2-5 points.)
+//
 // Tile of workgroup b under that deal: a bijection on [0, ntiles) that
 // permutes each complete group of 64 and leaves the last, partial group in
 // order (gridDim.x is the whole grid or the cap, a multiple of 64, so b mod 8
@@ -239,7 +249,7 @@ __global__ __launch_bounds__(kRcUnalignedBlock) void rc_unaligned_kernel(ReduceA
         src[k] = (const gf32x4u *)(a.src[k] + a.head);
 
     for (uint64_t b = blockIdx.x; b < ntiles; b += gridDim.x) {
-        const uint64_t t = rc_unaligned_map<N>() ? xcd_block_tile(b, ntiles) : b;
+        const uint64_t t = xcd_block_tile(b, ntiles);
         const uint64_t base = t * BS;
         const uint32_t nblk = (uint32_t)(nvec - base < (uint64_t)BS ? nvec - base : (uint64_t)BS);
         if (threadIdx.x < nblk) {
@@ -262,6 +272,106 @@ __global__ __launch_bounds__(kRcUnalignedBlock) void rc_unaligned_kernel(ReduceA
     // Up to 3 floats before the aligned body (threads 0-2) and 3 after it
     // (threads 32-34).
     static_assert(BS >= 64, "head and tail threads");
+    if (blockIdx.x == 0) {
+        gf32 *d = (gf32 *)(a.dst);
+        if (threadIdx.x < a.head) {
+            const uint64_t j = threadIdx.x;
+            d[j] = rc_sum_scalar<N>(a, j);
+        } else if (threadIdx.x >= 32 && threadIdx.x < 32 + a.tail) {
+            const uint64_t j = a.head + 4 * nvec + (threadIdx.x - 32);
+            d[j] = rc_sum_scalar<N>(a, j);
+        }
+    }
+}
+
+// Unaligned path from eight sources up, staged through LDS.  Every source is
+// read with aligned 16-byte loads straight into LDS (global_load_lds_dwordx4:
+// lane l's block lands 16 l bytes past the wave's LDS base), and the thread
+// that writes dst block i reads its source's four floats back from LDS at the
+// source's 4-byte offset s (0..3 floats): they lie in aligned blocks i and
+// i + 1 of the source's 16-byte-aligned view A = src + head - s.  A wave's
+// tile is 64 dst blocks, so it loads A's blocks i0 .. i0 + 63 plus the first
+// dwords of block i0 + 64.  That last load is made by the whole wave, one
+// dword per lane (lanes 3..63 all take dword 3): a load for lane 0 alone,
+// under an exec mask, was merged by the compiler with the next source's
+// full-wave load into one instruction whose LDS address came from lane 0.
+// Every load reads an aligned 16-byte block holding at least one of the
+// source's elements (indexes are clamped to the last such block), so no load
+// leaves the pages the source lies in.  Sources are staged G = rc_lds_group(N)
+// at a time and added in order as each group lands.
+// Measured on MI355X with sources 4 or 8 bytes off dst, at 256 MiB per
+// buffer: eight sources 72.5-73.9% of HBM peak against 70.0-70.4% with the
+// 4-byte-aligned loads, sixteen 74.0-74.5% against 69.8-70.0%, level with the
+// aligned path (74.1%); at 64 MiB per buffer 1.5-5.6 points ahead from nine to
+// sixteen sources, and 1-3 points behind below eight (four sources 76%
+// against 78%).  It reads 3.6-4.9% more bytes than the sources hold, as the
+// other form does (the line shared by two tiles): the gain is the loads that
+// no longer straddle two 16-byte blocks.
+template <int N>
+__global__ __launch_bounds__(kRcLdsBlock) void rc_unaligned_lds_kernel(ReduceArgs a) {
+    constexpr int G = rc_lds_group(N);
+    constexpr uint32_t kRegion = 64 * 4 + 64;   // dwords per staged source: 64 blocks, then block 64's dwords
+    __shared__ __attribute__((aligned(16))) uint32_t lds[G][kRegion];
+    typedef float f32x4l __attribute__((ext_vector_type(4), aligned(4)));
+    const uint32_t lane = threadIdx.x;
+    const uint32_t xdw = 4 * (lane < 3 ? lane : 3);   // this lane's dword of block i0 + 64
+    const uint64_t nvec = a.nvec;
+    const uint64_t ntiles = (nvec + kRcLdsBlock - 1) / kRcLdsBlock;
+    // Per source: the 16-byte-aligned view A, the offset s in floats, and the
+    // last block of A holding one of the source's elements (block nvec holds
+    // the body's last s floats when s > 0).  The compiler keeps these across
+    // the tile loop, in vector registers from nine sources up (83-147 VGPRs);
+    // a form that recomputed them per tile in scalar registers (42-70 VGPRs)
+    // ran 3-6 points slower.
+    uint64_t abase[N];
+    uint32_t sh[N];
+    uint64_t last[N];
+#pragma unroll
+    for (int k = 0; k < N; k++) {
+        const uint64_t p = reinterpret_cast<uint64_t>(a.src[k] + a.head);
+        sh[k] = (uint32_t)(p & 15) >> 2;
+        abase[k] = p - (p & 15);
+        last[k] = sh[k] != 0 ? nvec : nvec - 1;
+    }
+    for (uint64_t b = blockIdx.x; b < ntiles; b += gridDim.x) {
+        const uint64_t i0 = xcd_block_tile(b, ntiles) * kRcLdsBlock;
+        const uint32_t nblk = (uint32_t)(nvec - i0 < (uint64_t)kRcLdsBlock ? nvec - i0 : (uint64_t)kRcLdsBlock);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int g0 = 0; g0 < N; g0 += G) {
+#pragma unroll
+            for (int j = 0; j < G; j++) {
+                const int k = g0 + j;
+                if (k < N) {
+                    const uint64_t bl = i0 + lane < last[k] ? i0 + lane : last[k];
+                    const uint64_t bx = i0 + 64 < last[k] ? i0 + 64 : last[k];
+                    __builtin_amdgcn_global_load_lds((const gvoid *)(abase[k] + bl * 16), (svoid *)&lds[j][0], 16, 0,
+                                                     kPolNt);
+                    __builtin_amdgcn_global_load_lds((const gvoid *)(abase[k] + bx * 16 + xdw),
+                                                     (svoid *)&lds[j][64 * 4], 4, 0, kPolNt);
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0);   // the group's blocks are in LDS
+#pragma unroll
+            for (int j = 0; j < G; j++) {
+                const int k = g0 + j;
+                if (k < N) {
+                    const f32x4 v = *(const f32x4l *)((const float *)&lds[j][0] + lane * 4 + sh[k]);
+                    acc = k == 0 ? v : acc + v;
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0);   // LDS read before the next group overwrites it
+        }
+        if (lane < nblk) {
+            const __amdgpu_buffer_rsrc_t out =
+                buffer_over(reinterpret_cast<uint64_t>(a.dst + a.head) + i0 * 16, nblk * 16u);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), out, lane * 16, 0,
+                                                   rc_store_pol(N));
+        }
+    }
+
+    // Up to 3 floats before the aligned body (threads 0-2) and 3 after it
+    // (threads 32-34).
     if (blockIdx.x == 0) {
         gf32 *d = (gf32 *)(a.dst);
         if (threadIdx.x < a.head) {
@@ -309,6 +419,8 @@ int reduce_grid(uint64_t nfloats, int nsrc, bool vector_path, int cu_count) {
         per_block = (uint64_t)kRcBlock * 4;
     else if (vector_path)
         per_block = (uint64_t)rc_block_of(nsrc) * 4;
+    else if (rc_unaligned_lds(nsrc))
+        per_block = (uint64_t)kRcLdsBlock * 4;
     else
         per_block = (uint64_t)kRcUnalignedBlock * 4;
     // one workgroup per tile, capped; the kernels loop when the cap binds
@@ -355,7 +467,10 @@ template <int N>
 static hipError_t launch_n(const ReduceArgs &a, bool vector_path, int grid, hipStream_t s) {
     if (vector_path)
         return launch(rc_vec_kernel<N>, grid, rc_block_of(N), s, nullptr, a);
-    return launch(rc_unaligned_kernel<N>, grid, kRcUnalignedBlock, s, nullptr, a);
+    if constexpr (rc_unaligned_lds(N))
+        return launch(rc_unaligned_lds_kernel<N>, grid, kRcLdsBlock, s, nullptr, a);
+    else
+        return launch(rc_unaligned_kernel<N>, grid, kRcUnalignedBlock, s, nullptr, a);
 }
 
 hipError_t launch_reduce_copy(const ReduceArgs &a, int nsrc, bool vector_path, int cu_count,

@@ -159,8 +159,10 @@ int tb_prep_sources(float *dev_base, uint64_t slice_stride_bytes, uint64_t k,
  * dst: device pointer to nfloats floats; srcs: HOST array of nsrc device
  * pointers (read during the call only).  All pointers 4-byte aligned.  When
  * every source shares dst's address modulo 16 the sources are read as aligned
- * 16-byte vectors; otherwise each source is read with 16-byte loads at its own
- * 4-byte alignment (3-7 points of HBM peak slower at 256 MiB).
+ * 16-byte vectors; otherwise, up to seven sources, each is read with 16-byte
+ * loads at its own 4-byte alignment, and from eight up with aligned 16-byte
+ * loads staged through LDS and read back at its offset (0-6 points of HBM peak
+ * slower than aligned at 256 MiB per buffer).
  * dst may be exactly equal to a source; any other overlap between dst and a
  * source is rejected.  Enqueues one kernel on `stream`.  nfloats == 0 is a
  * no-op.

@@ -2,8 +2,9 @@
 kernels cap their grid at 2^20 workgroups and loop over the tiles beyond it:
 the memset's 4 KiB tiles pass the cap above 4 GiB, the vector path's 1 KiB
 tiles (one or two sources) above 1 GiB per buffer and its 2 KiB tiles (three
-sources and more) above 2 GiB, and the unaligned path's 2 KiB tiles (any
-source count) above 2 GiB.  The oracle's
+sources and more) above 2 GiB, the unaligned path's 2 KiB tiles (up to seven
+sources) above 2 GiB and its LDS-staged 1 KiB tiles (eight and more) above
+1 GiB.  The oracle's
 definitions hold at any size and are checked as such: every byte of a memset
 is the memset byte and a one-source reduce-copy equals its source bitwise
 (both on the device), and every element of a multi-source sum equals the
@@ -105,6 +106,7 @@ def test_reduce2_above_4GiB_every_element():
     (3, (96 << 20) + 5, 4, 0),     # 384 MiB + 20 B per source: above the memory-side cache's size
     (2, (1 << 29) + 261, 0, 4),    # 2 GiB + 1,044 B, sources 4 / 8 B off dst: the unaligned path past the cap
     (5, (1 << 29) + 261, 0, 4),    # the same with sources 4/8/12/0/4 B off
+    (9, (1 << 28) + 261, 0, 4),    # 1 GiB + 1,044 B, nine sources off dst: the LDS-staged path's 1 KiB tiles past the cap
 ])
 def test_reduce_multi_source_large_every_element(nsrc, n, offset, src_step):
     torch = require_gpu()

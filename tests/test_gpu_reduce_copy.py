@@ -84,14 +84,16 @@ def test_reduce_copy_mixed_offsets_all_n(nsrc, dst_off, n):
     assert dbuf.guards_intact()
 
 
-@pytest.mark.parametrize("nsrc", [1, 2, 3, 4, 16])
+@pytest.mark.parametrize("nsrc", [1, 2, 3, 4, 7, 8, 9, 12, 16])
 @pytest.mark.parametrize("body_blocks", [1, 63, 64, 65, 127, 128, 129, 255, 256, 257])
 @pytest.mark.parametrize("tail", [0, 3])
 def test_reduce_copy_unaligned_tile_edges(nsrc, body_blocks, tail):
     """Unaligned path (sources 4, 8, 12, 0 bytes off dst) with the float4 body
-    ending on, just before and just after the edges of a wave and of a
-    128-block tile, two tiles in: the last thread's 16-byte loads end exactly
-    at the sources' last body elements."""
+    ending on, just before and just after the edges of a wave and of a tile
+    (128 blocks up to seven sources; 64-block one-wave tiles staged through LDS
+    from eight up), past the first 256 blocks: the last thread's 16-byte loads
+    end exactly at the sources' last body elements, and the LDS path's clamp
+    to the last source block is exercised at every offset."""
     torch = require_gpu()
     tile = 128
     n = 4 * (2 * tile + body_blocks) + tail
