@@ -152,7 +152,7 @@ def test_reduce_copy_memset_byte(mb):
     assert dbuf.guards_intact()
 
 
-@pytest.mark.parametrize("nsrc,other_off", [(1, 0), (2, 0), (3, 0), (16, 0), (2, 4), (3, 8), (5, 12), (16, 4)])
+@pytest.mark.parametrize("nsrc,other_off", [(1, 0), (2, 0), (3, 0), (16, 0), (2, 4), (3, 8), (5, 12), (8, 8), (9, 12), (16, 4)])
 def test_reduce_copy_in_place_alias(nsrc, other_off):
     """dst == src0 exactly: every element is read before it is written.  With
     the other sources off dst's alignment the unaligned path runs, with the
