@@ -222,9 +222,11 @@ def main_line(args, torch, tb, wl):
     b = setup_batch(torch, tb, batch, wl.DEFAULT_ROTATE_BYTES, BATCH_DST_ROTATE_BYTES)
     # The destination rotates too, by the slice rule over DST_ROTATE_BYTES: at
     # 256 MiB per buffer the source rule gives K = 1, and a fixed 256 MiB
-    # destination stays in the 256 MB memory-side cache, which then absorbs
-    # its rewrites; over K_d slices every launch writes lines no recent launch
-    # wrote, so the timed rate is the HBM rate.
+    # destination written with stores that allocate in the 256 MB memory-side
+    # cache stays there and has its rewrites absorbed; over K_d slices every
+    # launch writes lines no recent launch wrote, so the timed rate is the HBM
+    # rate whatever the store policy (the library's stores do not allocate
+    # there, and the fixed-destination pass beside it reads the same).
     kd = tb.tb_num_slices(rs.num_bytes, DST_ROTATE_BYTES)
     dsts = torch.zeros(kd * rs.stride // 4, dtype=torch.float32, device="cuda")
     dst_base = int(dsts.data_ptr())
@@ -306,9 +308,9 @@ def main_line(args, torch, tb, wl):
                             "ms_max": round(max(rc_ms), 5), "gbps": round(rc_gbps, 1),
                             "frac_of_peak": round(rc_gbps / HBM_PEAK_GBPS, 4),
                             "fixed_dst": {
-                                "note": "the same steps with one fixed destination, as the pages time it: the "
-                                        "256 MiB destination then stays in the 256 MB memory-side cache, which "
-                                        "absorbs part of its rewrites (not an HBM rate)",
+                                "note": "the same steps with one fixed destination, as the pages time it; the "
+                                        "reduce-copy's stores do not allocate in the 256 MB memory-side cache, so "
+                                        "a rewritten destination is not served from it and this too is an HBM rate",
                                 "ms_mean": round(statistics.mean(rc_fixed_ms), 5),
                                 "frac_of_peak": round(rc_bytes / (statistics.mean(rc_fixed_ms) * 1e-3) / 1e9
                                                       / HBM_PEAK_GBPS, 4)}},
