@@ -996,9 +996,10 @@ def roofs(args, torch, tb, wl):
       1. streams larger than the 256 MB memory-side cache: read-only (the
          instrument, and torch's sum), write-only (both store policies, the
          library's memset, torch's fill) and a 512 MiB copy;
-      2. N + 1 streams of 64 MiB rotated over 4 slices read at once against
-         the reduce-copy with N sources (N reads, one write, destination
-         rotated the same way);
+      2. N + 1 streams of 64 MiB rotated over 4 slices read at once, and N
+         streams read with their XOR written to one more (the reduce-copy's
+         own pattern with integer work only), against the reduce-copy with N
+         sources (N reads, one write, destination rotated the same way);
       3. C4's 47,520 copies cut into <= 4 KiB tiles on the host (the same
          bytes, source replicas and destination pools as the bench step): tile
          copy, destinations written only, sources read only, against the
@@ -1068,6 +1069,14 @@ def roofs(args, torch, tb, wl):
         line("instrument", f"read-only, {k} streams of 64 MiB rotated over 4 slices",
              loop_us([lambda i=i, k=k: rf.tbr_read([b + (i % kslices) * nb for b in base[:k]], nb, sh)
                       for i in range(n)]), k * nb, streams=k)
+        # the reduce-copy's own pattern: nsrc streams read, one written (their
+        # XOR), with the library's store policy for that source count
+        pol, pname = ((rf.TBR_STORE_STREAMING, "nt sc0 sc1") if nsrc <= 2 else (rf.TBR_STORE_NT, "nt"))
+        line("instrument", f"{nsrc} streams read, their XOR written to one more ({pname} stores), 64 MiB each, "
+             "rotated over 4 slices",
+             loop_us([lambda i=i, nsrc=nsrc, pol=pol: rf.tbr_combine([b + (i % kslices) * nb for b in base[:nsrc]],
+                                                                    dbase + (i % kslices) * nb, nb, pol, sh)
+                      for i in range(n)]), (nsrc + 1) * nb, streams=nsrc + 1, nsrc=nsrc)
         line("library", f"tb_reduce_copy nsrc={nsrc}, 64 MiB per buffer, sources and destination rotated over 4 "
              "slices", loop_us([lambda i=i, nsrc=nsrc: tb.tb_reduce_copy(
                  dbase + (i % kslices) * nb, [b + (i % kslices) * nb for b in base[:nsrc]], nb // 4, sh)

@@ -92,6 +92,27 @@ __global__ __launch_bounds__(kBlock) void copy_kernel(uint64_t dst, uint64_t src
     }
 }
 
+// dst = the XOR of K sources, 16 bytes per thread and buffer: the
+// reduce-copy's access pattern (K streams read, one written) with integer
+// work only.
+template <int K, int POL>
+__global__ __launch_bounds__(kBlock) void combine_kernel(Bufs b, uint64_t dst, uint64_t bytes) {
+    const uint64_t ntiles = (bytes + kTile - 1) / kTile;
+    for (uint64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const uint64_t off = t * kTile;
+        const uint32_t len = (uint32_t)(bytes - off < kTile ? bytes - off : kTile);
+        u32x4 v[K];
+#pragma unroll
+        for (int k = 0; k < K; k++)
+            v[k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc(b.p[k] + off, len), threadIdx.x * 16, 0, kNt);
+        u32x4 x = v[0];
+#pragma unroll
+        for (int k = 1; k < K; k++)
+            x ^= v[k];
+        __builtin_amdgcn_raw_buffer_store_b128(x, rsrc(dst + off, len), threadIdx.x * 16, 0, POL);
+    }
+}
+
 __device__ __forceinline__ bool tile_ok(uint64_t src, uint64_t dst, uint32_t bytes) {
     return bytes >= 16 && bytes <= kTile && (bytes & 15u) == 0 && ((src | dst) & 15u) == 0;
 }
@@ -173,8 +194,33 @@ template <int K>
 void launch_write_pol(const Bufs &b, uint64_t bytes, uint32_t word, uint32_t policy, hipStream_t s) {
     if (policy == TBR_STORE_DEVICE)
         launch_write<K, kSc1>(b, bytes, word, s);
+    else if (policy == TBR_STORE_NT)
+        launch_write<K, kNt>(b, bytes, word, s);
     else
         launch_write<K, kNt | kSc0 | kSc1>(b, bytes, word, s);
+}
+
+template <int K>
+void launch_combine(const Bufs &b, uint64_t dst, uint64_t bytes, uint32_t policy, hipStream_t s) {
+    const dim3 grid(grid_for((bytes + kTile - 1) / kTile)), block(kBlock);
+    if (policy == TBR_STORE_DEVICE)
+        hipLaunchKernelGGL((combine_kernel<K, kSc1>), grid, block, 0, s, b, dst, bytes);
+    else if (policy == TBR_STORE_NT)
+        hipLaunchKernelGGL((combine_kernel<K, kNt>), grid, block, 0, s, b, dst, bytes);
+    else
+        hipLaunchKernelGGL((combine_kernel<K, kNt | kSc0 | kSc1>), grid, block, 0, s, b, dst, bytes);
+}
+
+// K in [1, TBR_MAX_BUFS - 1] by a compile-time table
+template <int K>
+void dispatch_combine(int32_t nsrcs, const Bufs &b, uint64_t dst, uint64_t bytes, uint32_t policy, hipStream_t s) {
+    if constexpr (K < TBR_MAX_BUFS) {
+        if (nsrcs == K) {
+            launch_combine<K>(b, dst, bytes, policy, s);
+            return;
+        }
+        dispatch_combine<K + 1>(nsrcs, b, dst, bytes, policy, s);
+    }
 }
 
 // K in [1, TBR_MAX_BUFS] by a compile-time table
@@ -213,7 +259,7 @@ int tbr_write(void *const *bufs, int32_t nbufs, uint64_t bytes_each, uint32_t wo
               void *stream) {
     tbr::Bufs b;
     if (!tbr::gather(const_cast<const void *const *>(bufs), nbufs, &b) || (bytes_each & 15u) != 0 ||
-        policy > TBR_STORE_STREAMING)
+        policy > TBR_STORE_NT)
         return TBR_ERR_INVALID;
     if (bytes_each == 0)
         return TBR_OK;
@@ -223,7 +269,7 @@ int tbr_write(void *const *bufs, int32_t nbufs, uint64_t bytes_each, uint32_t wo
 
 int tbr_copy(void *dst, const void *src, uint64_t bytes, uint32_t policy, void *stream) {
     const uint64_t d = reinterpret_cast<uint64_t>(dst), sa = reinterpret_cast<uint64_t>(src);
-    if (policy > TBR_STORE_STREAMING || (bytes & 15u) != 0)
+    if (policy > TBR_STORE_NT || (bytes & 15u) != 0)
         return TBR_ERR_INVALID;
     if (bytes == 0)
         return TBR_OK;
@@ -233,15 +279,33 @@ int tbr_copy(void *dst, const void *src, uint64_t bytes, uint32_t policy, void *
     const dim3 grid(tbr::grid_for((bytes + tbr::kTile - 1) / tbr::kTile));
     if (policy == TBR_STORE_DEVICE)
         hipLaunchKernelGGL(tbr::copy_kernel<tbr::kSc1>, grid, dim3(tbr::kBlock), 0, s, d, sa, bytes);
+    else if (policy == TBR_STORE_NT)
+        hipLaunchKernelGGL(tbr::copy_kernel<tbr::kNt>, grid, dim3(tbr::kBlock), 0, s, d, sa, bytes);
     else
         hipLaunchKernelGGL(tbr::copy_kernel<tbr::kNt | tbr::kSc0 | tbr::kSc1>, grid, dim3(tbr::kBlock), 0, s, d, sa,
                            bytes);
     return tbr::hip_status(hipGetLastError(), "copy launch");
 }
 
+int tbr_combine(const void *const *srcs, int32_t nsrcs, void *dst, uint64_t bytes_each, uint32_t policy,
+                void *stream) {
+    tbr::Bufs b;
+    const uint64_t d = reinterpret_cast<uint64_t>(dst);
+    if (nsrcs < 1 || nsrcs >= TBR_MAX_BUFS || !tbr::gather(srcs, nsrcs, &b) || (bytes_each & 15u) != 0 ||
+        policy > TBR_STORE_NT || d == 0 || (d & 15u) != 0)
+        return TBR_ERR_INVALID;
+    if (bytes_each == 0)
+        return TBR_OK;
+    for (int32_t k = 0; k < nsrcs; k++)
+        if (b.p[k] < d + bytes_each && d < b.p[k] + bytes_each)
+            return TBR_ERR_INVALID;
+    tbr::dispatch_combine<1>(nsrcs, b, d, bytes_each, policy, static_cast<hipStream_t>(stream));
+    return tbr::hip_status(hipGetLastError(), "combine launch");
+}
+
 static int tiles_launch(int mode, const tbr_tile *tiles_dev, uint32_t ntiles, uint32_t word, uint32_t policy,
                         void *stream) {
-    if (policy > TBR_STORE_STREAMING)
+    if (policy > TBR_STORE_NT)
         return TBR_ERR_INVALID;
     if (ntiles == 0)
         return TBR_OK;
@@ -250,13 +314,16 @@ static int tiles_launch(int mode, const tbr_tile *tiles_dev, uint32_t ntiles, ui
     const tbr::Tile *t = reinterpret_cast<const tbr::Tile *>(tiles_dev);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const dim3 grid(tbr::grid_for(ntiles)), block(tbr::kBlock);
-    constexpr int kDev = tbr::kSc1, kStr = tbr::kNt | tbr::kSc0 | tbr::kSc1;
-    const bool dev = policy == TBR_STORE_DEVICE;
+    constexpr int kDev = tbr::kSc1, kStr = tbr::kNt | tbr::kSc0 | tbr::kSc1, kNtOnly = tbr::kNt;
     void (*kernel)(const tbr::Tile *, uint32_t, uint32_t);
     if (mode == 0)
-        kernel = dev ? tbr::tiles_kernel<0, kDev> : tbr::tiles_kernel<0, kStr>;
+        kernel = policy == TBR_STORE_DEVICE ? tbr::tiles_kernel<0, kDev>
+                 : policy == TBR_STORE_NT   ? tbr::tiles_kernel<0, kNtOnly>
+                                            : tbr::tiles_kernel<0, kStr>;
     else if (mode == 1)
-        kernel = dev ? tbr::tiles_kernel<1, kDev> : tbr::tiles_kernel<1, kStr>;
+        kernel = policy == TBR_STORE_DEVICE ? tbr::tiles_kernel<1, kDev>
+                 : policy == TBR_STORE_NT   ? tbr::tiles_kernel<1, kNtOnly>
+                                            : tbr::tiles_kernel<1, kStr>;
     else
         kernel = tbr::tiles_kernel<2, kStr>;
     hipLaunchKernelGGL(kernel, grid, block, 0, s, t, ntiles, word);

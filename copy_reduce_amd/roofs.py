@@ -14,12 +14,12 @@ from ._tb import PKG
 ROOFS_LIB_PATH = os.path.join(PKG, "libtb_roofs.so")
 
 TBR_OK, TBR_ERR_INVALID, TBR_ERR_HIP = 0, -1, -2
-TBR_STORE_DEVICE, TBR_STORE_STREAMING = 0, 1
+TBR_STORE_DEVICE, TBR_STORE_STREAMING, TBR_STORE_NT = 0, 1, 2
 TBR_MAX_BUFS = 17
 TILE_BYTES = 4096
 
-EXPORTS = ("tbr_read", "tbr_write", "tbr_copy", "tbr_tiles_copy", "tbr_tiles_write", "tbr_tiles_read",
-           "tbr_last_hip_error")
+EXPORTS = ("tbr_read", "tbr_write", "tbr_copy", "tbr_combine", "tbr_tiles_copy", "tbr_tiles_write",
+           "tbr_tiles_read", "tbr_last_hip_error")
 
 if not os.path.exists(ROOFS_LIB_PATH):
     raise ImportError(f"{ROOFS_LIB_PATH} is missing: build the HIP libraries first "
@@ -31,6 +31,7 @@ _SIGS = {
     "tbr_read": (ctypes.c_int, [_vp, _i32, _u64, _vp]),
     "tbr_write": (ctypes.c_int, [_vp, _i32, _u64, _u32, _u32, _vp]),
     "tbr_copy": (ctypes.c_int, [_vp, _vp, _u64, _u32, _vp]),
+    "tbr_combine": (ctypes.c_int, [_vp, _i32, _vp, _u64, _u32, _vp]),
     "tbr_tiles_copy": (ctypes.c_int, [_vp, _u32, _u32, _vp]),
     "tbr_tiles_write": (ctypes.c_int, [_vp, _u32, _u32, _u32, _vp]),
     "tbr_tiles_read": (ctypes.c_int, [_vp, _u32, _vp]),
@@ -66,6 +67,10 @@ def tbr_write(buf_ptrs, bytes_each: int, word: int, policy: int, stream: int) ->
 
 def tbr_copy(dst_ptr: int, src_ptr: int, nbytes: int, policy: int, stream: int) -> None:
     _check("tbr_copy", lib.tbr_copy(dst_ptr, src_ptr, nbytes, policy, stream))
+
+
+def tbr_combine(src_ptrs, dst_ptr: int, bytes_each: int, policy: int, stream: int) -> None:
+    _check("tbr_combine", lib.tbr_combine(_ptrs(src_ptrs), len(src_ptrs), dst_ptr, bytes_each, policy, stream))
 
 
 def tbr_tiles_copy(tiles_dev_ptr: int, ntiles: int, policy: int, stream: int) -> None:

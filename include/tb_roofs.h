@@ -8,8 +8,9 @@
  * bytes came from a cache).  These kernels give that allowance for the access
  * patterns libtb's kernels run, so a kernel's rate can be read against the
  * rate of its pattern rather than against the HBM peak alone:
- *   - read-only and write-only streams over 1 .. 17 buffers at once (the
- *     reduce-copy with N sources reads N streams and writes one);
+ *   - read-only and write-only streams over 1 .. 17 buffers at once, and
+ *     N streams read with their XOR written to one more (the reduce-copy with
+ *     N sources reads N streams and writes one);
  *   - copies, writes and reads of a list of tiles of at most 4 KiB whose
  *     addresses the host computed beforehand (a batch of scattered copies cut
  *     into tiles: the batched copy's exact bytes and destinations, with none
@@ -41,7 +42,8 @@ enum {
 /* Store cache policy of the write and copy instruments. */
 enum {
     TBR_STORE_DEVICE = 0,      /* device scope (sc1): allocates in the memory-side cache */
-    TBR_STORE_STREAMING = 1    /* nontemporal, system scope (nt sc0 sc1): does not       */
+    TBR_STORE_STREAMING = 1,   /* nontemporal, system scope (nt sc0 sc1): does not       */
+    TBR_STORE_NT = 2           /* nontemporal (nt): does not                             */
 };
 
 /* Most buffers one read or write instrument takes. */
@@ -85,6 +87,19 @@ int tbr_write(void *const *bufs, int32_t nbufs, uint64_t bytes_each, uint32_t wo
  * `policy`.  Errors as tbr_write.
  */
 int tbr_copy(void *dst, const void *src, uint64_t bytes, uint32_t policy, void *stream);
+
+/*
+ * dst = the XOR of nsrcs buffers of bytes_each bytes, all at once: tile t of
+ * every source (4 KiB) read by workgroup t with nontemporal 16-byte loads,
+ * and tile t of dst written with `policy` stores.  The reduce-copy's access
+ * pattern (nsrcs streams read, one written) with integer work only.
+ * srcs: HOST array of nsrcs device pointers; nsrcs in [1, TBR_MAX_BUFS - 1];
+ * every pointer 16-byte aligned and bytes_each a multiple of 16; dst must not
+ * overlap a source.  Errors: TBR_ERR_INVALID for any of that or an unknown
+ * policy; TBR_ERR_HIP.  bytes_each == 0 is a no-op.
+ */
+int tbr_combine(const void *const *srcs, int32_t nsrcs, void *dst, uint64_t bytes_each, uint32_t policy,
+                void *stream);
 
 /*
  * Over a DEVICE array of ntiles tiles (each as tbr_tile states; tiles whose

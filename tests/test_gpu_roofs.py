@@ -54,6 +54,28 @@ def test_copy_equals_source():
         assert torch.equal(dst[:nbytes], src) and bool((dst[nbytes:] == 0).all())
 
 
+def test_combine_writes_the_xor_of_its_sources():
+    """tbr_combine (N streams read, their XOR written to one more): every
+    16-byte word of dst is the XOR of the sources' words, computed here with
+    numpy on the host, and nothing past dst's end is written."""
+    torch = require_gpu()
+    import copy_reduce_amd.roofs as rf
+    sh = torch.cuda.current_stream().cuda_stream
+    rng = np.random.default_rng(8)
+    for nsrc, nbytes, pol in ((1, 4096 * 3 + 16, rf.TBR_STORE_NT), (2, 4096 * 33 + 48, rf.TBR_STORE_STREAMING),
+                              (9, 1 << 20, rf.TBR_STORE_DEVICE), (16, 4096 * 5 + 272, rf.TBR_STORE_NT)):
+        note(f"roofs: combine {nsrc} sources of {nbytes} B policy {pol}")
+        host = [rng.integers(0, 256, size=nbytes, dtype=np.uint8) for _ in range(nsrc)]
+        srcs = [torch.from_numpy(h).cuda() for h in host]
+        dst = torch.zeros(nbytes + 64, dtype=torch.uint8, device="cuda")
+        rf.tbr_combine([int(x.data_ptr()) for x in srcs], int(dst.data_ptr()), nbytes, pol, sh)
+        torch.cuda.synchronize()
+        exp = np.bitwise_xor.reduce(np.stack(host), axis=0)
+        got = dst.cpu().numpy()
+        oracle.assert_equal(got[:nbytes], exp, f"combine nsrc={nsrc}")
+        assert not got[nbytes:].any()
+
+
 @pytest.mark.parametrize("placement", ["random_slots", "packed"])
 def test_tile_copy_of_c4_equals_oracle(placement):
     """C4's copies (in a 256 MiB pool) cut into tiles and copied by the

@@ -40,13 +40,23 @@ def test_roofs_argument_checks():
     assert lib.tbr_read(rf._ptrs([0x1008]), 1, 4096, None) == rf.TBR_ERR_INVALID      # misaligned
     assert lib.tbr_read(bufs, 1, 4100, None) == rf.TBR_ERR_INVALID                     # not a multiple of 16
     assert lib.tbr_read(bufs, 1, 0, None) == rf.TBR_OK
-    assert lib.tbr_write(bufs, 1, 4096, 0, 2, None) == rf.TBR_ERR_INVALID               # unknown policy
+    assert lib.tbr_write(bufs, 1, 4096, 0, 3, None) == rf.TBR_ERR_INVALID               # unknown policy
+    two = rf._ptrs([0x1000, 0x3000])
+    assert lib.tbr_combine(two, 2, 0x5000, 4096, 3, None) == rf.TBR_ERR_INVALID          # unknown policy
+    assert lib.tbr_combine(two, 2, 0x3800, 4096, 0, None) == rf.TBR_ERR_INVALID          # dst overlaps a source
+    assert lib.tbr_combine(two, 2, 0x5008, 4096, 0, None) == rf.TBR_ERR_INVALID          # misaligned dst
+    assert lib.tbr_combine(two, 2, None, 4096, 0, None) == rf.TBR_ERR_INVALID
+    assert lib.tbr_combine(two, 0, 0x5000, 4096, 0, None) == rf.TBR_ERR_INVALID
+    assert lib.tbr_combine(rf._ptrs([0x1000] * 17), 17, 0x90000, 4096, 0, None) == rf.TBR_ERR_INVALID
+    assert lib.tbr_combine(two, 2, 0x5000, 4100, 0, None) == rf.TBR_ERR_INVALID          # not a multiple of 16
+    assert lib.tbr_combine(two, 2, 0x5000, 0, 2, None) == rf.TBR_OK
     assert lib.tbr_copy(0x1800, 0x1000, 4096, 0, None) == rf.TBR_ERR_INVALID            # overlapping
     assert lib.tbr_copy(0x2000, 0x1008, 16, 0, None) == rf.TBR_ERR_INVALID              # misaligned
     assert lib.tbr_copy(0x2000, 0x1000, 0, 0, None) == rf.TBR_OK
     assert lib.tbr_tiles_copy(None, 5, 0, None) == rf.TBR_ERR_INVALID
     assert lib.tbr_tiles_copy(0x1004, 5, 0, None) == rf.TBR_ERR_INVALID
     assert lib.tbr_tiles_write(0x1000, 5, 0, 7, None) == rf.TBR_ERR_INVALID
+    assert lib.tbr_tiles_copy(0x1000, 5, 3, None) == rf.TBR_ERR_INVALID
     assert lib.tbr_tiles_read(None, 0, None) == rf.TBR_OK
 
 
