@@ -9,8 +9,9 @@
  * binary32; a batched copy of 1,000 copies of 1 B - 4 KiB at arbitrary byte
  * offsets through tb_batched_copy (with and without a workgroup cap),
  * tb_batched_copy_noalloc and both kinds of descriptor-slot ring; the spin
- * gate, the launch-carried timing events, the launch figures, and the
- * argument checks.  Prints "capi ok" and exits 0 on success.
+ * gate, the launch-carried timing events, the launch figures, the memset
+ * form, the recovery-mode hook, the status strings and the argument checks.
+ * Prints "capi ok" and exits 0 on success.
  */
 #include <stdint.h>
 #include <stdio.h>
@@ -173,6 +174,39 @@ static int check_rotation(hipStream_t s) {
     return 0;
 }
 
+/* The memset form (N = 0 with an explicit byte), the recovery-mode hook and
+ * the status strings. */
+static int check_misc(hipStream_t s) {
+    const uint64_t n = 4099;
+    uint8_t *d, *h = malloc(n * 4);
+    if (!h)
+        return 1;
+    HIP_OK(hipMalloc((void **)&d, n * 4 + 8));
+    HIP_OK(hipMemset(d, 0x11, n * 4 + 8));
+    TB_OK_(tb_reduce_copy_ex((float *)(d + 4), NULL, 0, n, 0x5Au, s));
+    HIP_OK(hipStreamSynchronize(s));
+    HIP_OK(hipMemcpy(h, d + 4, n * 4, hipMemcpyDeviceToHost));
+    for (uint64_t i = 0; i < n * 4; i++)
+        if (h[i] != 0x5A) {
+            fprintf(stderr, "memset: byte %llu is %u\n", (unsigned long long)i, h[i]);
+            return 1;
+        }
+    if (tb_reduce_copy_ex((float *)d, NULL, 0, 16, 256u, s) != TB_ERR_INVALID ||
+        tb_batched_set_mode(7) != TB_ERR_INVALID) {
+        fprintf(stderr, "accepted an invalid memset byte or mode\n");
+        return 1;
+    }
+    TB_OK_(tb_batched_set_mode(TB_BC_NO_WAIT));
+    TB_OK_(tb_batched_set_mode(TB_BC_NORMAL));
+    if (tb_status_string(TB_ERR_TIMEOUT)[0] == '\0' || tb_last_hip_error() == NULL) {
+        fprintf(stderr, "empty status string\n");
+        return 1;
+    }
+    HIP_OK(hipFree(d));
+    free(h);
+    return 0;
+}
+
 /* The spin gate, launch-carried events and launch figures. */
 static int check_gate_and_timing(hipStream_t s) {
     float *a, *b;
@@ -306,7 +340,8 @@ int main(void) {
     HIP_OK(hipSetDevice(0));
     hipStream_t s;
     HIP_OK(hipStreamCreate(&s));
-    if (check_reduce(s) != 0 || check_rotation(s) != 0 || check_gate_and_timing(s) != 0 || check_batch(s) != 0)
+    if (check_reduce(s) != 0 || check_rotation(s) != 0 || check_misc(s) != 0 || check_gate_and_timing(s) != 0 ||
+        check_batch(s) != 0)
         return 1;
     HIP_OK(hipStreamDestroy(s));
     TB_OK_(tb_shutdown());

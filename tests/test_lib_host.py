@@ -242,3 +242,15 @@ def test_product_package_does_not_use_oracle():
                 assert "oracle" not in text.lower(), f
     text = open(os.path.join(ROOT, "oracle", "oracle.c")).read() + open(os.path.join(ROOT, "oracle", "__init__.py")).read()
     assert "copy_reduce_amd" not in text.replace("(copy_reduce_amd/)", "") and "tb.h" not in text
+
+
+def test_c_consumer_calls_every_entry_point():
+    """tests/capi/capi_check.c (run on the GPU by test_gpu_capi.py) calls every
+    entry point include/tb.h declares, so the whole boundary is exercised once
+    from plain C without the Python binding."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    header = open(os.path.join(root, "include", "tb.h")).read()
+    consumer = open(os.path.join(root, "tests", "capi", "capi_check.c")).read()
+    declared = sorted(set(re.findall(r"^(?:int|const char \*)\s*(tb_\w+)\s*\(", header, re.M)))
+    assert declared
+    assert [d for d in declared if d + "(" not in consumer] == []
